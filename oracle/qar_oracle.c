@@ -1,0 +1,226 @@
+/*
+ * qar_oracle.c -- plain, slow CPU oracle for dynamic block-wise int8
+ * quantization and quantized reduction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this file's shared object; the library under
+ * block_wise_int8_amd/ never does, and this file shares no code, header or
+ * constant with it.
+ *
+ * What it follows.  "EQuARX: Efficient Quantized AllReduce in XLA for
+ * Distributed Machine Learning Acceleration" (page summary on shd-paper.top):
+ *   - section "technical framework", step 1: the input is cut into blocks;
+ *   - step 2: each block is quantized dynamically from BF16 or FP32 to INT8;
+ *   - step 3: the AllReduce runs on the quantized data (the summation is
+ *     where error builds up: same page, "problem definition", and the
+ *     abstract);
+ *   - step 4: the result is dequantized back to the original type;
+ *   - section "key design", item 1: each block's range is found at run time.
+ * The pages leave the arithmetic open.  The readings taken here:
+ *   scale  s   = fl32(absmax / 127)            one IEEE fp32 division
+ *   code   q_i = 0                              if s == 0
+ *              = clamp(rne(fl32(x_i / s)), -127, 127)   otherwise
+ *   value  y_i = fl32((float)q_i * s)           dequantize
+ *   reduce acc = y_0, then acc = fl32(acc + y_r) for r = 1..N-1 (rank
+ *          order, separate multiply and add), then quantize(acc)
+ *   ring   quantize(fl32(y_in + x_local))
+ *   bf16   round-to-nearest-even of the fp32 value to 8 significant bits.
+ * Inputs must be finite; the oracle refuses NaN and infinity.
+ *
+ * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared.
+ * x86-64 SSE arithmetic (FLT_EVAL_METHOD == 0): every float operation below
+ * rounds once to binary32, round-to-nearest-even, with gradual underflow.
+ *
+ * Every function works on host memory, any block length >= 1, and a
+ * partial last block (its absmax covers only its own elements).
+ */
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if FLT_EVAL_METHOD != 0
+#error "the oracle needs binary32 evaluation of float expressions"
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1 };
+enum { ORACLE_OK = 0, ORACLE_BAD_ARG = -1, ORACLE_NONFINITE = -2 };
+
+/* bf16 is the top half of a binary32 word, so widening is exact. */
+static float bf16_bits_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a finite binary32 value to the nearest bfloat16, ties to the even
+ * neighbour.  The magnitude bits are rounded; the sign bit rides along. */
+static uint16_t float_to_bf16_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t upper = u >> 16;        /* truncated bf16 pattern          */
+    uint32_t rest = u & 0xFFFFu;     /* dropped low half of the pattern */
+    if (rest > 0x8000u || (rest == 0x8000u && (upper & 1u)))
+        upper += 1u;                 /* carries into the exponent as IEEE does */
+    return (uint16_t)upper;
+}
+
+static float load_element(const void* x, int dtype, size_t i)
+{
+    if (dtype == ORACLE_BF16)
+        return bf16_bits_to_float(((const uint16_t*)x)[i]);
+    return ((const float*)x)[i];
+}
+
+/* Quantize one block of `len` fp32 values: writes len codes and one scale. */
+static void quantize_one_block(const float* v, size_t len, int8_t* q, float* scale)
+{
+    float absmax = 0.0f;
+    for (size_t i = 0; i < len; i++) {
+        float m = fabsf(v[i]);
+        if (m > absmax)
+            absmax = m;
+    }
+    float s = absmax / 127.0f;
+    *scale = s;
+    for (size_t i = 0; i < len; i++) {
+        if (s == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        float t = v[i] / s;
+        float r = nearbyintf(t); /* default rounding mode: to nearest, ties even */
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -127.0f)
+            r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+}
+
+static size_t block_count(size_t n, size_t block) { return (n + block - 1) / block; }
+
+static float dequant_value(int8_t q, float s) { return (float)q * s; }
+
+/* x: n elements of dtype (bf16 as raw uint16 patterns, or fp32).
+ * codes: int8[n]; scales: fp32[ceil(n / block)]. */
+int oracle_quantize(const void* x, int dtype, size_t n, size_t block,
+                    int8_t* codes, float* scales)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!x || !codes || !scales)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(x, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* v = malloc(block * sizeof *v);
+    if (!v)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            v[i] = load_element(x, dtype, start + i);
+        quantize_one_block(v, len, codes + start, scales + b);
+    }
+    free(v);
+    return ORACLE_OK;
+}
+
+/* out: fp32[n] = (float)code * scale of its block. */
+int oracle_dequantize_f32(const int8_t* codes, const float* scales, size_t n,
+                          size_t block, float* out)
+{
+    if (block == 0)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++)
+        out[i] = dequant_value(codes[i], scales[i / block]);
+    return ORACLE_OK;
+}
+
+/* out: bf16[n] patterns, the fp32 dequantized value rounded to bf16. */
+int oracle_dequantize_bf16(const int8_t* codes, const float* scales, size_t n,
+                           size_t block, uint16_t* out)
+{
+    if (block == 0)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++)
+        out[i] = float_to_bf16_bits(dequant_value(codes[i], scales[i / block]));
+    return ORACLE_OK;
+}
+
+/* One-shot N-way reduce.  codes[r] / scales[r] hold rank r's quantized
+ * buffer (n codes, ceil(n/block) scales).  Each element is the fp32 sum of
+ * the dequantized contributions taken in rank order 0, 1, ..., N-1; the sum
+ * is then quantized again per block. */
+int oracle_reduce(const int8_t* const* codes, const float* const* scales,
+                  size_t nranks, size_t n, size_t block,
+                  int8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || nranks == 0)
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value(codes[0][start + i], scales[0][b]);
+        for (size_t r = 1; r < nranks; r++)
+            for (size_t i = 0; i < len; i++)
+                acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);
+        quantize_one_block(acc, len, codes_out + start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}
+
+/* One ring step: dequantize the incoming buffer, add this rank's own
+ * unquantized values (bf16 or fp32), quantize the sum per block. */
+int oracle_ring_step(const int8_t* codes_in, const float* scales_in,
+                     const void* local, int dtype, size_t n, size_t block,
+                     int8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(local, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value(codes_in[start + i], scales_in[b]) +
+                     load_element(local, dtype, start + i);
+        quantize_one_block(acc, len, codes_out + start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}
+
+/* The bf16 rounding on its own, so that tests can pin it to a library
+ * conversion. */
+void oracle_f32_to_bf16(const float* in, size_t n, uint16_t* out)
+{
+    for (size_t i = 0; i < n; i++)
+        out[i] = float_to_bf16_bits(in[i]);
+}

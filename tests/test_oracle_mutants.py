@@ -1,0 +1,57 @@
+"""Planted mistakes: each test copies the oracle's C source, plants one
+plausible mistake (a wrong rounding, scale, index, sign, operand, order or a
+dropped term), builds the copy with gcc and checks that at least one pin of
+``tests/pins.py`` fails on it.  The real oracle is never modified.  No GPU."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
+    "scale_over_128": ("float s = absmax / 127.0f;", "float s = absmax / 128.0f;"),
+    "scale_by_reciprocal": ("float s = absmax / 127.0f;", "float s = absmax * (1.0f / 127.0f);"),
+    "quotient_by_reciprocal": ("float t = v[i] / s;", "float t = v[i] * (1.0f / s);"),
+    "clamp_to_minus_128": ("if (r < -127.0f)\n            r = -127.0f;",
+                           "if (r < -128.0f)\n            r = -128.0f;"),
+    "no_clamp": ("if (r > 127.0f)\n            r = 127.0f;\n        if (r < -127.0f)\n            r = -127.0f;\n",
+                 ""),
+    "zero_rule_on_absmax": ("if (s == 0.0f) {", "if (absmax == 0.0f) {"),
+    "absmax_without_abs": ("float m = fabsf(v[i]);", "float m = v[i];"),
+    "reduce_drops_last_rank": ("for (size_t r = 1; r < nranks; r++)", "for (size_t r = 1; r + 1 < nranks; r++)"),
+    "reduce_rank_order": ("acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);",
+                          "acc[i] = acc[i] + dequant_value(codes[nranks - r][start + i], scales[nranks - r][b]);"),
+    "reduce_fma": ("acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);",
+                   "acc[i] = fmaf((float)codes[r][start + i], scales[r][b], acc[i]);"),
+    "dequant_scale_index": ("out[i] = dequant_value(codes[i], scales[i / block]);",
+                            "out[i] = dequant_value(codes[i], scales[(i / block) & ~(size_t)1]);"),
+    "ring_subtracts_local": ("scales_in[b]) +\n", "scales_in[b]) -\n"),
+    "ring_first_scale": ("acc[i] = dequant_value(codes_in[start + i], scales_in[b]) +",
+                         "acc[i] = dequant_value(codes_in[start + i], scales_in[0]) +"),
+    "ring_local_as_bf16": ("load_element(local, dtype, start + i);", "load_element(local, ORACLE_BF16, start + i);"),
+    "bf16_ties_away": ("if (rest > 0x8000u || (rest == 0x8000u && (upper & 1u)))", "if (rest >= 0x8000u)"),
+    "bf16_truncates": ("upper += 1u;", "upper += 0u;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique in the oracle source"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(str(path), str(tmp_path / f"lib{name}.so"))
+    mutant = oracle.Oracle(lib)
+    caught = None
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError) as e:
+            caught = (pin.__name__, str(e)[:120])
+            break
+    assert caught is not None, f"no pin catches the planted mistake {name}"
+    print(f"{name}: caught by {caught[0]} ({caught[1]})")
+    os.remove(lib)
