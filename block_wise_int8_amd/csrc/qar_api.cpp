@@ -1,0 +1,239 @@
+// qar_api.cpp -- the C ABI of libqar (declared in include/qar.h):
+// synchronous argument checks, then one launch on the caller's stream.
+// Nothing here allocates device memory or synchronizes.
+#include "qar.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <stdio.h>
+#include <string.h>
+
+#include "qar_launch.h"
+
+static_assert(QAR_MAX_RANKS == qar::kMaxRanks, "rank limit mismatch");
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+qar_status hip_fail(hipError_t e, const char* where) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+    return QAR_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool block_supported(uint32_t b) { return b == 64 || b == 128 || b == 256; }
+
+size_t dtype_bytes(qar_dtype d) { return d == QAR_BF16 ? 2 : 4; }
+
+bool dtype_ok(qar_dtype d) { return d == QAR_BF16 || d == QAR_F32; }
+
+struct Range {
+    uintptr_t lo, hi; // [lo, hi)
+};
+
+Range range(const void* p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// An output may coincide exactly with an input it is allowed to replace;
+// any other overlap is an error.
+bool bad_overlap(Range out, Range in, bool same_allowed) {
+    if (!overlap(out, in)) return false;
+    return !(same_allowed && out.lo == in.lo && out.hi == in.hi);
+}
+
+// Checks common to every call: sizes, block, alignment of codes/scales.
+qar_status check_common(size_t n, uint32_t block) {
+    if (!block_supported(block)) return QAR_ERR_UNSUPPORTED;
+    if (n % block != 0 || n > QAR_MAX_ELEMENTS) return QAR_ERR_INVALID_ARG;
+    return QAR_OK;
+}
+
+qar_status check_reduce(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
+                        uint32_t block, int8_t* codes_out, float* scales_out, void* out,
+                        qar_dtype out_dtype) {
+    qar_status st = check_common(n, block);
+    if (st != QAR_OK) return st;
+    if (!codes || !scales || !codes_out || !scales_out) return QAR_ERR_INVALID_ARG;
+    if (nranks == 0 || nranks > QAR_MAX_RANKS) return QAR_ERR_INVALID_ARG;
+    if (out && !dtype_ok(out_dtype)) return QAR_ERR_UNSUPPORTED;
+    const size_t nb = n / block;
+    if (!aligned(codes_out, 16) || !aligned(scales_out, 4) || (out && !aligned(out, 16)))
+        return QAR_ERR_MISALIGNED;
+    const Range co = range(codes_out, n), so = range(scales_out, nb * 4);
+    if (overlap(co, so)) return QAR_ERR_INVALID_ARG;
+    Range oo{0, 0};
+    if (out) {
+        oo = range(out, n * dtype_bytes(out_dtype));
+        if (overlap(oo, co) || overlap(oo, so)) return QAR_ERR_INVALID_ARG;
+    }
+    int same_codes = -1, same_scales = -1;
+    for (uint32_t r = 0; r < nranks; ++r) {
+        if (!codes[r] || !scales[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(codes[r], 16) || !aligned(scales[r], 4)) return QAR_ERR_MISALIGNED;
+        const Range ci = range(codes[r], n), si = range(scales[r], nb * 4);
+        if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci))
+            return QAR_ERR_INVALID_ARG;
+        if (out && (overlap(oo, ci) || overlap(oo, si))) return QAR_ERR_INVALID_ARG;
+        if (co.lo == ci.lo) same_codes = (int)r;
+        if (so.lo == si.lo) same_scales = (int)r;
+    }
+    // in place means codes AND scales of the same rank
+    if (same_codes != same_scales) return QAR_ERR_INVALID_ARG;
+    return QAR_OK;
+}
+
+void fill_ranks(qar::RankPtrs& rp, const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                size_t elem_offset, size_t block_offset) {
+    memset(&rp, 0, sizeof rp);
+    for (uint32_t r = 0; r < nranks; ++r) {
+        rp.codes[r] = codes[r] + elem_offset;
+        rp.scales[r] = scales[r] + block_offset;
+    }
+}
+
+int out_kind(const void* out, qar_dtype d) {
+    if (!out) return qar::kOutNone;
+    return d == QAR_BF16 ? qar::kOutBF16 : qar::kOutF32;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* qar_status_string(qar_status s) {
+    switch (s) {
+    case QAR_OK: return "ok";
+    case QAR_ERR_INVALID_ARG: return "invalid argument";
+    case QAR_ERR_MISALIGNED: return "misaligned pointer";
+    case QAR_ERR_UNSUPPORTED: return "unsupported block size or dtype";
+    case QAR_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* qar_last_error(void) { return g_last_error; }
+
+qar_status qar_quantize_blocks(const void* x, qar_dtype dtype, size_t n, uint32_t block, int8_t* codes,
+                               float* scales, void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_common(n, block);
+    if (st != QAR_OK) return st;
+    if (!x || !codes || !scales) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QAR_ERR_MISALIGNED;
+    const Range xi = range(x, n * dtype_bytes(dtype)), co = range(codes, n),
+                so = range(scales, n / block * 4);
+    if (overlap(xi, co) || overlap(xi, so) || overlap(co, so)) return QAR_ERR_INVALID_ARG;
+    const hipError_t e = qar::launch_quantize(x, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, n,
+                                              (int)block, codes, scales, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_quantize_blocks");
+}
+
+qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* out,
+                                qar_dtype out_dtype, void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
+    if (st != QAR_OK) return st;
+    qar::RankPtrs rp;
+    fill_ranks(rp, codes, scales, nranks, 0, 0);
+    const hipError_t e = qar::launch_reduce(rp, (int)nranks, n, (int)block, codes_out, scales_out, out,
+                                            out_kind(out, out_dtype), (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized");
+}
+
+qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
+                                          uint32_t nranks, size_t n, uint32_t block, int8_t* codes_out,
+                                          float* scales_out, void* out, qar_dtype out_dtype,
+                                          uint32_t nchunks, void* const* streams, uint32_t nstreams,
+                                          void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
+    if (st != QAR_OK) return st;
+    if (nchunks == 0 || !streams || nstreams == 0 || nstreams > QAR_MAX_STREAMS) return QAR_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nstreams; ++i)
+        if (!streams[i]) return QAR_ERR_INVALID_ARG;
+
+    const size_t nb = n / block;
+    const size_t chunks = nchunks < nb ? nchunks : nb;
+    const size_t per = (nb + chunks - 1) / chunks; // blocks per chunk
+    const hipStream_t main_st = (hipStream_t)stream;
+    const int kind = out_kind(out, out_dtype);
+    const size_t out_bytes = out ? (out_dtype == QAR_BF16 ? 2 : 4) : 0;
+    const uint32_t used = (uint32_t)(chunks < nstreams ? chunks : nstreams);
+
+    hipEvent_t start, done[QAR_MAX_STREAMS];
+    hipError_t e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    uint32_t made = 0;
+    for (; made < used; ++made) {
+        e = hipEventCreateWithFlags(&done[made], hipEventDisableTiming);
+        if (e != hipSuccess) break;
+    }
+    if (e == hipSuccess) e = hipEventRecord(start, main_st);
+    for (uint32_t i = 0; e == hipSuccess && i < used; ++i)
+        e = hipStreamWaitEvent((hipStream_t)streams[i], start, 0);
+    for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
+        const size_t b0 = c * per;
+        if (b0 >= nb) break;
+        const size_t bn = (nb - b0 < per) ? nb - b0 : per;
+        const size_t e0 = b0 * block;
+        qar::RankPtrs rp;
+        fill_ranks(rp, codes, scales, nranks, e0, b0);
+        void* out_c = out ? (void*)((char*)out + e0 * out_bytes) : nullptr;
+        e = qar::launch_reduce(rp, (int)nranks, bn * block, (int)block, codes_out + e0, scales_out + b0,
+                               out_c, kind, (hipStream_t)streams[c % used]);
+    }
+    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) {
+        e = hipEventRecord(done[i], (hipStream_t)streams[i]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, done[i], 0);
+    }
+    // Events may be destroyed while pending; HIP releases them on completion.
+    (void)hipEventDestroy(start);
+    for (uint32_t i = 0; i < made; ++i) (void)hipEventDestroy(done[i]);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_pipelined");
+}
+
+qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, qar_dtype dtype,
+                         size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_common(n, block);
+    if (st != QAR_OK) return st;
+    if (!codes_in || !scales_in || !local || !codes_out || !scales_out) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (!aligned(codes_in, 16) || !aligned(codes_out, 16) || !aligned(local, 16) || !aligned(scales_in, 4) ||
+        !aligned(scales_out, 4))
+        return QAR_ERR_MISALIGNED;
+    const size_t nb = n / block;
+    const Range ci = range(codes_in, n), si = range(scales_in, nb * 4), li = range(local, n * dtype_bytes(dtype)),
+                co = range(codes_out, n), so = range(scales_out, nb * 4);
+    if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci) ||
+        overlap(co, li) || overlap(so, li) || overlap(co, so))
+        return QAR_ERR_INVALID_ARG;
+    if ((co.lo == ci.lo) != (so.lo == si.lo)) return QAR_ERR_INVALID_ARG;
+    const hipError_t e =
+        qar::launch_ring_step(codes_in, scales_in, local, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, n,
+                              (int)block, codes_out, scales_out, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_ring_step");
+}
+
+qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                          qar_dtype out_dtype, void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_common(n, block);
+    if (st != QAR_OK) return st;
+    if (!codes || !scales || !out) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(out_dtype)) return QAR_ERR_UNSUPPORTED;
+    if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16)) return QAR_ERR_MISALIGNED;
+    const Range ci = range(codes, n), si = range(scales, n / block * 4),
+                oo = range(out, n * dtype_bytes(out_dtype));
+    if (overlap(oo, ci) || overlap(oo, si)) return QAR_ERR_INVALID_ARG;
+    const hipError_t e = qar::launch_dequantize(codes, scales, n, (int)block, out, out_kind(out, out_dtype),
+                                                (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_dequantize");
+}
+
+} // extern "C"

@@ -1,0 +1,263 @@
+// qar_kernels.hip -- libqar's gfx950 kernels and their launchers.
+//
+// Method: EQuARX ("EQuARX: Efficient Quantized AllReduce in XLA for
+// Distributed Machine Learning Acceleration"), page summary, section
+// "technical framework": blocks (step 1), dynamic per-block quantization to
+// INT8 (step 2, with the run-time range of "key design" item 1), reduction of
+// quantized contributions (step 3), dequantization (step 4).  The arithmetic
+// each kernel performs is spelled out in include/qar.h.
+//
+// Every kernel streams HBM once: 16-byte loads and stores per lane, a block's
+// absmax by DPP inside its lanes, the requantization fused behind the
+// reduction so the fp32 sum never leaves registers.  A workgroup walks tiles
+// of 4096 elements with a grid-stride loop (the grid is capped, the loop
+// covers any n).
+#include "qar_device.h"
+#include "qar_launch.h"
+
+namespace qar {
+
+// ---------------------------------------------------------------------------
+// quantize: x (bf16 or fp32) -> codes, scales
+
+template <int B, typename In>
+__global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x, size_t n,
+                                                       int8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       uint32_t ntiles) {
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
+        const bool valid = e0 < n;
+        float v[kLaneElems];
+        if (valid) {
+            load16(x + e0, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) v[i] = 0.0f;
+        }
+        const float s = block_max<B>(lane_absmax(v)) / 127.0f;
+        const uint4 q = quantize16(v, s);
+        if (valid) {
+            store_b128(codes + e0, q);
+            if (e0 % B == 0) scales[e0 / B] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// one-shot reduce: N quantized ranks -> requantized sum (+ optional dequant)
+
+template <int B>
+__global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, size_t n,
+                                                     int8_t* codes_out, float* scales_out,
+                                                     void* __restrict__ out, int out_kind,
+                                                     uint32_t ntiles) {
+    constexpr int G = 8; // ranks whose loads are in flight together
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
+        const bool valid = e0 < n;
+        const size_t blk = e0 / B;
+        float acc[kLaneElems];
+        for (int g = 0; g < nranks; g += G) {
+            uint4 q[G];
+            float s[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                q[j] = make_uint4(0u, 0u, 0u, 0u);
+                s[j] = 0.0f;
+                if (g + j < nranks && valid) {
+                    q[j] = load_b128(rp.codes[g + j] + e0);
+                    s[j] = rp.scales[g + j][blk];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (g + j < nranks) {
+                    float y[kLaneElems];
+                    dequantize16(q[j], s[j], y);
+                    if (g + j == 0) {
+#pragma unroll
+                        for (int i = 0; i < kLaneElems; ++i) acc[i] = y[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + y[i];
+                    }
+                }
+            }
+        }
+        const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
+        const uint4 qo = quantize16(acc, so);
+        if (valid) {
+            store_b128(codes_out + e0, qo);
+            if (e0 % B == 0) scales_out[blk] = so;
+            if (out_kind != kOutNone) {
+                float y[kLaneElems];
+                dequantize16(qo, so, y);
+                if (out_kind == kOutBF16)
+                    store16(static_cast<uint16_t*>(out) + e0, y);
+                else
+                    store16(static_cast<float*>(out) + e0, y);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ring step: dequantize incoming + add local (bf16/fp32) + requantize
+
+template <int B, typename In>
+__global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, const float* scales_in,
+                                                        const In* __restrict__ local, size_t n,
+                                                        int8_t* codes_out, float* scales_out,
+                                                        uint32_t ntiles) {
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
+        const bool valid = e0 < n;
+        const size_t blk = e0 / B;
+        float acc[kLaneElems];
+        if (valid) {
+            const uint4 q = load_b128(codes_in + e0);
+            const float s = scales_in[blk];
+            float x[kLaneElems];
+            load16(local + e0, x);
+            dequantize16(q, s, acc);
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + x[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) acc[i] = 0.0f;
+        }
+        const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
+        const uint4 qo = quantize16(acc, so);
+        if (valid) {
+            store_b128(codes_out + e0, qo);
+            if (e0 % B == 0) scales_out[blk] = so;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dequantize: codes, scales -> bf16 or fp32
+
+template <int B, typename Out>
+__global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restrict__ codes,
+                                                         const float* __restrict__ scales, size_t n,
+                                                         Out* __restrict__ out, uint32_t ntiles) {
+    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
+        if (e0 >= n) continue;
+        const uint4 q = load_b128(codes + e0);
+        const float s = scales[e0 / B];
+        float y[kLaneElems];
+        dequantize16(q, s, y);
+        store16(out + e0, y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+namespace {
+
+constexpr uint32_t kMaxGrid = 1u << 22;
+
+struct Grid {
+    uint32_t ntiles, blocks;
+};
+
+Grid grid_for(size_t n) {
+    const size_t tiles = (n + kTileElems - 1) / kTileElems;
+    Grid g;
+    g.ntiles = (uint32_t)tiles;
+    g.blocks = (uint32_t)(tiles < kMaxGrid ? tiles : kMaxGrid);
+    return g;
+}
+
+template <int B>
+hipError_t quantize_b(const void* x, int in_kind, size_t n, int8_t* codes, float* scales, hipStream_t st) {
+    const Grid g = grid_for(n);
+    if (in_kind == kInBF16)
+        hipLaunchKernelGGL((k_quantize<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st,
+                           static_cast<const uint16_t*>(x), n, codes, scales, g.ntiles);
+    else
+        hipLaunchKernelGGL((k_quantize<B, float>), dim3(g.blocks), dim3(kThreads), 0, st,
+                           static_cast<const float*>(x), n, codes, scales, g.ntiles);
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t reduce_b(const RankPtrs& rp, int nranks, size_t n, int8_t* codes_out, float* scales_out,
+                    void* out, int out_kind, hipStream_t st) {
+    const Grid g = grid_for(n);
+    hipLaunchKernelGGL((k_reduce<B>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n, codes_out,
+                       scales_out, out, out_kind, g.ntiles);
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
+                  size_t n, int8_t* codes_out, float* scales_out, hipStream_t st) {
+    const Grid g = grid_for(n);
+    if (in_kind == kInBF16)
+        hipLaunchKernelGGL((k_ring_step<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+                           scales_in, static_cast<const uint16_t*>(local), n, codes_out, scales_out,
+                           g.ntiles);
+    else
+        hipLaunchKernelGGL((k_ring_step<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+                           scales_in, static_cast<const float*>(local), n, codes_out, scales_out,
+                           g.ntiles);
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void* out, int out_kind,
+                        hipStream_t st) {
+    const Grid g = grid_for(n);
+    if (out_kind == kOutBF16)
+        hipLaunchKernelGGL((k_dequantize<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, codes,
+                           scales, n, static_cast<uint16_t*>(out), g.ntiles);
+    else
+        hipLaunchKernelGGL((k_dequantize<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, codes, scales,
+                           n, static_cast<float*>(out), g.ntiles);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
+                           hipStream_t st) {
+    switch (block) {
+    case 64: return quantize_b<64>(x, in_kind, n, codes, scales, st);
+    case 128: return quantize_b<128>(x, in_kind, n, codes, scales, st);
+    default: return quantize_b<256>(x, in_kind, n, codes, scales, st);
+    }
+}
+
+hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
+                         float* scales_out, void* out, int out_kind, hipStream_t st) {
+    switch (block) {
+    case 64: return reduce_b<64>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
+    case 128: return reduce_b<128>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
+    default: return reduce_b<256>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
+    }
+}
+
+hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
+                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st) {
+    switch (block) {
+    case 64: return ring_b<64>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
+    case 128: return ring_b<128>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
+    default: return ring_b<256>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
+    }
+}
+
+hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,
+                             int out_kind, hipStream_t st) {
+    switch (block) {
+    case 64: return dequantize_b<64>(codes, scales, n, out, out_kind, st);
+    case 128: return dequantize_b<128>(codes, scales, n, out, out_kind, st);
+    default: return dequantize_b<256>(codes, scales, n, out, out_kind, st);
+    }
+}
+
+} // namespace qar

@@ -1,0 +1,32 @@
+// qar_launch.h -- internal interface between the C ABI (qar_api.cpp) and the
+// kernel launchers (qar_kernels.hip).  Arguments reaching these functions
+// have already been validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qar {
+
+constexpr int kMaxRanks = 32;
+
+enum : int { kInBF16 = 0, kInF32 = 1 };
+enum : int { kOutNone = -1, kOutBF16 = 0, kOutF32 = 1 };
+
+// Rank pointers travel in the kernel's argument segment (512 bytes).
+struct RankPtrs {
+    const int8_t* codes[kMaxRanks];
+    const float* scales[kMaxRanks];
+};
+
+hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
+                           hipStream_t st);
+hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
+                         float* scales_out, void* out, int out_kind, hipStream_t st);
+hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
+                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st);
+hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,
+                             int out_kind, hipStream_t st);
+
+} // namespace qar

@@ -1,0 +1,209 @@
+"""ctypes binding of libqar (include/qar.h): argument marshalling only.
+
+Every computation runs in libqar's HIP kernels; this module turns torch
+tensors into device pointers, HIP streams into handles, allocates outputs
+with torch when the caller passes none, and raises ``QarError`` on a
+non-OK status.  A missing library raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libqar.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "qar.h")
+
+QAR_OK, QAR_ERR_INVALID_ARG, QAR_ERR_MISALIGNED, QAR_ERR_UNSUPPORTED, QAR_ERR_HIP = range(5)
+QAR_BF16, QAR_F32 = 0, 1
+QAR_MAX_RANKS = 32
+QAR_MAX_STREAMS = 16
+BLOCK_SIZES = (64, 128, 256)
+
+_vp, _sz, _u32, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
+
+_SIGNATURES = {
+    "qar_quantize_blocks": [_vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_reduce_quantized": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_reduce_quantized_pipelined": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _u32, _vp, _u32, _vp],
+    "qar_ring_step": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_dequantize": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
+    "qar_status_string": [_int],
+    "qar_last_error": [],
+}
+
+
+class QarError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        L = lib()
+        text = L.qar_status_string(status).decode()
+        detail = L.qar_last_error().decode() if status == QAR_ERR_HIP else ""
+        super().__init__(f"{where}: {text}" + (f" ({detail})" if detail else ""))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqar (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"libqar is not built: {LIBRARY} is missing "
+                               "(build it with __graft_entry__.build() or block_wise_int8_amd/build.py)")
+        L = ctypes.CDLL(LIBRARY)
+        for name, args in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name in ("qar_status_string", "qar_last_error") else _int
+        _lib = L
+    return _lib
+
+
+def declared_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions include/qar.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qar_\w+)\s*\(", text, re.M)))
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return QAR_BF16
+    if dt == torch.float32:
+        return QAR_F32
+    raise TypeError(f"libqar handles bfloat16 and float32 data, not {dt}")
+
+
+def _dev(t: torch.Tensor, what: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _check(status: int, where: str) -> None:
+    if status != QAR_OK:
+        raise QarError(status, where)
+
+
+def _ptrs(ts: list[torch.Tensor]):
+    arr = (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    return arr
+
+
+# ----------------------------------------------------------------------------
+# the calls
+
+
+def qar_quantize_blocks(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
+                        scales: torch.Tensor | None = None, stream=None):
+    """x (bf16/fp32, any shape, contiguous) -> (codes int8[n], scales fp32[n/block])."""
+    _dev(x, "x")
+    n = x.numel()
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(max(n // block, 1), dtype=torch.float32, device=x.device)
+    _check(lib().qar_quantize_blocks(x.data_ptr(), _dtype_code(x.dtype), n, block,
+                                     _dev(codes, "codes").data_ptr(), _dev(scales, "scales").data_ptr(),
+                                     _stream(stream)), "qar_quantize_blocks")
+    return codes, scales
+
+
+def _out_args(out: torch.Tensor | None):
+    if out is None:
+        return None, QAR_BF16
+    _dev(out, "out")
+    return out.data_ptr(), _dtype_code(out.dtype)
+
+
+def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
+                         codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, stream=None):
+    """One-shot N-way reduce of rank-ordered (codes, scales) -> (codes_out, scales_out);
+    ``out`` (optional bf16/fp32 tensor) receives the dequantized result."""
+    if len(codes) != len(scales) or not codes:
+        raise ValueError("need one scales tensor per codes tensor, at least one rank")
+    n = codes[0].numel()
+    for c, s in zip(codes, scales):
+        _dev(c, "codes[r]"), _dev(s, "scales[r]")
+    dev = codes[0].device
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=torch.int8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
+    optr, odt = _out_args(out)
+    cp, sp = _ptrs(codes), _ptrs(scales)
+    _check(lib().qar_reduce_quantized(ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), len(codes), n, block,
+                                      _dev(codes_out, "codes_out").data_ptr(),
+                                      _dev(scales_out, "scales_out").data_ptr(), optr, odt,
+                                      _stream(stream)), "qar_reduce_quantized")
+    return codes_out, scales_out
+
+
+def qar_reduce_quantized_pipelined(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
+                                   nchunks: int, streams: list, codes_out: torch.Tensor | None = None,
+                                   scales_out: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                                   stream=None):
+    """The reduce cut into ``nchunks`` chunks enqueued round-robin on ``streams``."""
+    if len(codes) != len(scales) or not codes:
+        raise ValueError("need one scales tensor per codes tensor, at least one rank")
+    n = codes[0].numel()
+    dev = codes[0].device
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=torch.int8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
+    optr, odt = _out_args(out)
+    cp, sp = _ptrs(codes), _ptrs(scales)
+    sts = (ctypes.c_void_p * len(streams))(*[_stream(s) for s in streams])
+    _check(lib().qar_reduce_quantized_pipelined(
+        ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), len(codes), n, block,
+        _dev(codes_out, "codes_out").data_ptr(), _dev(scales_out, "scales_out").data_ptr(), optr, odt,
+        nchunks, ctypes.cast(sts, _vp), len(streams), _stream(stream)), "qar_reduce_quantized_pipelined")
+    return codes_out, scales_out
+
+
+def qar_ring_step(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
+                  codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
+    """quantize(dequantize(codes_in, scales_in) + local) -> (codes_out, scales_out).
+    Pass codes_out=codes_in, scales_out=scales_in to work in place."""
+    _dev(codes_in, "codes_in"), _dev(scales_in, "scales_in"), _dev(local, "local")
+    n = codes_in.numel()
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=torch.int8, device=codes_in.device)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=codes_in.device)
+    _check(lib().qar_ring_step(codes_in.data_ptr(), scales_in.data_ptr(), local.data_ptr(),
+                               _dtype_code(local.dtype), n, block, _dev(codes_out, "codes_out").data_ptr(),
+                               _dev(scales_out, "scales_out").data_ptr(), _stream(stream)), "qar_ring_step")
+    return codes_out, scales_out
+
+
+def qar_dequantize(codes: torch.Tensor, scales: torch.Tensor, block: int, out: torch.Tensor | None = None,
+                   out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """codes, scales -> out (bf16 or fp32)."""
+    _dev(codes, "codes"), _dev(scales, "scales")
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _check(lib().qar_dequantize(codes.data_ptr(), scales.data_ptr(), n, block, _dev(out, "out").data_ptr(),
+                                _dtype_code(out.dtype), _stream(stream)), "qar_dequantize")
+    return out

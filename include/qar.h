@@ -1,0 +1,168 @@
+/*
+ * qar.h -- C ABI of libqar: dynamic block-wise int8 quantization and
+ * quantized reduction, one GPU's share of a quantized AllReduce, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method is EQuARX ("EQuARX: Efficient Quantized AllReduce in XLA for
+ * Distributed Machine Learning Acceleration"; page summary, section
+ * "technical framework", steps 1-4; section "key design", item 1): the
+ * tensor is cut into blocks, each block is quantized from BF16/FP32 to INT8
+ * with a range found at run time, the AllReduce sums the quantized
+ * contributions, and the result is dequantized back to the original type.
+ * The pages leave the arithmetic open; libqar fixes it as follows, for every
+ * call, bit for bit:
+ *
+ *   scale  s   = absmax / 127            one IEEE binary32 division
+ *   code   q_i = 0 if s == 0, else clamp(rne(x_i / s), -127, 127)
+ *                (x_i / s is the correctly rounded binary32 quotient; rne
+ *                rounds to the nearest integer, ties to even; -128 is
+ *                never produced)
+ *   value  y_i = (float)q_i * s           one binary32 multiply
+ *   bf16   round-to-nearest-even of the binary32 value
+ *
+ * All binary32 arithmetic rounds to nearest even with gradual underflow (no
+ * flush to zero); multiplies and adds are never fused.
+ *
+ * Layout.  A buffer of n elements is nb = n / block consecutive blocks of
+ * `block` elements (row-major flattening; for a [rows, hidden] tensor with
+ * hidden % block == 0 the blocks run along the hidden dimension).  Codes are
+ * int8[n] in element order; scales are a separate float[nb], one per block,
+ * in block order.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers owned by the caller.  libqar never
+ *     allocates, frees or synchronizes device memory.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
+ *     passed as void*; NULL is the default stream) and the call returns.
+ *   - Arguments are checked before anything is enqueued.  A failed check
+ *     returns a QAR_ERR_* status and enqueues nothing.  A failed launch
+ *     returns QAR_ERR_HIP; qar_last_error() then names the HIP error.
+ *   - n == 0 is a valid empty call: QAR_OK, nothing enqueued, no pointer is
+ *     read.
+ *   - Requirements: block is 64, 128 or 256; n % block == 0;
+ *     n <= QAR_MAX_ELEMENTS; element and code pointers 16-byte aligned;
+ *     scale pointers 4-byte aligned.
+ *   - Inputs must be finite.  Output for NaN or infinite input is
+ *     unspecified (it is not checked, for speed).
+ *   - Output buffers must not overlap input buffers, except where a call
+ *     says otherwise.  Partial overlap is rejected with QAR_ERR_INVALID_ARG.
+ *   - Any block-aligned sub-range of a valid call (pointers advanced by
+ *     k*block elements and k scales) is itself a valid call with the same
+ *     results in that range.
+ *   - Thread-safe; the only global state is a per-device cache of the
+ *     compute-unit count.
+ */
+#ifndef QAR_H
+#define QAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qar_status {
+    QAR_OK = 0,
+    QAR_ERR_INVALID_ARG = 1, /* null pointer, n % block != 0, bad rank count, overlap */
+    QAR_ERR_MISALIGNED = 2,  /* a pointer breaks the alignment rule above */
+    QAR_ERR_UNSUPPORTED = 3, /* block size or dtype outside what is built */
+    QAR_ERR_HIP = 4          /* the HIP runtime refused a launch or call */
+} qar_status;
+
+typedef enum qar_dtype {
+    QAR_BF16 = 0, /* bfloat16, stored as 16-bit patterns */
+    QAR_F32 = 1   /* IEEE binary32 */
+} qar_dtype;
+
+#define QAR_MAX_RANKS 32
+#define QAR_MAX_ELEMENTS ((size_t)1 << 40)
+#define QAR_MAX_STREAMS 16
+
+/*
+ * Per-block dynamic quantization ("technical framework" steps 1-2; "key
+ * design" item 1).
+ *   x       [in]  n elements of `dtype`.
+ *   codes   [out] int8[n].
+ *   scales  [out] float[n / block].
+ */
+qar_status qar_quantize_blocks(const void* x, qar_dtype dtype, size_t n, uint32_t block,
+                               int8_t* codes, float* scales, void* stream);
+
+/*
+ * One-shot N-way reduce of quantized contributions, then requantization of
+ * the sum ("technical framework" step 3: the AllReduce works on the
+ * quantized data; the error that summation builds up is the problem the
+ * abstract and the "problem definition" section name).  For each element:
+ *   acc = y_0;  acc = acc + y_r for r = 1 .. nranks-1  (binary32, rank order)
+ * and the result is quantize(acc) per block.
+ *   codes, scales  [in]  HOST arrays of nranks DEVICE pointers, rank order;
+ *                        codes[r] is int8[n], scales[r] is float[n/block].
+ *   nranks         1 .. QAR_MAX_RANKS.
+ *   codes_out      [out] int8[n];  scales_out [out] float[n/block].  These
+ *                  may be exactly the buffers of one input rank (in place).
+ *   out            [out, optional] NULL, or n elements of out_dtype that
+ *                  receive dequantize(codes_out, scales_out) -- step 4,
+ *                  fused.  It is the requantized result, not the raw sum, so
+ *                  that every rank of a real AllReduce dequantizes identical
+ *                  bits.
+ */
+qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* scales,
+                                uint32_t nranks, size_t n, uint32_t block,
+                                int8_t* codes_out, float* scales_out,
+                                void* out, qar_dtype out_dtype, void* stream);
+
+/*
+ * The same reduce, cut into `nchunks` block-aligned chunks that are
+ * enqueued round-robin on `streams[0 .. nstreams-1]`, so that one chunk's
+ * loads overlap another chunk's arithmetic (the pages' pipelining of
+ * communication and compute, "key innovations" item 2 and "key design"
+ * item 3, taken on one GPU).  Results are bit-identical to
+ * qar_reduce_quantized for every nchunks and nstreams.  Work on the side
+ * streams starts after everything already enqueued on `stream`, and
+ * `stream` waits for all chunks, so the caller sees one ordered operation on
+ * `stream`.  The call creates and releases its HIP events.
+ *   nchunks   >= 1 (clipped to the number of blocks).
+ *   streams   HOST array of nstreams hipStream_t (as void*), 1 .. QAR_MAX_STREAMS.
+ */
+qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
+                                          uint32_t nranks, size_t n, uint32_t block,
+                                          int8_t* codes_out, float* scales_out,
+                                          void* out, qar_dtype out_dtype,
+                                          uint32_t nchunks, void* const* streams,
+                                          uint32_t nstreams, void* stream);
+
+/*
+ * One ring step: dequantize the incoming quantized buffer, add this rank's
+ * own unquantized values, requantize ("technical framework" step 3 taken as
+ * a ring; the error accumulates over the N-1 steps):
+ *   acc_i = y_in,i + x_local,i   (binary32), then quantize(acc) per block.
+ *   codes_in, scales_in  [in]  int8[n], float[n/block].
+ *   local                [in]  n elements of `dtype` (bf16 or fp32).
+ *   codes_out, scales_out [out] int8[n], float[n/block]; may be exactly
+ *                        codes_in / scales_in (in place).
+ */
+qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in,
+                         const void* local, qar_dtype dtype, size_t n, uint32_t block,
+                         int8_t* codes_out, float* scales_out, void* stream);
+
+/*
+ * Dequantize back to the original type ("technical framework" step 4):
+ *   out_i = (float)q_i * s_b, stored as binary32 or rounded to bf16.
+ *   codes, scales  [in]  int8[n], float[n/block].
+ *   out            [out] n elements of out_dtype.
+ */
+qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, uint32_t block,
+                          void* out, qar_dtype out_dtype, void* stream);
+
+/* Static text for a status code. */
+const char* qar_status_string(qar_status status);
+
+/* Text of the last QAR_ERR_HIP raised on the calling thread ("" if none). */
+const char* qar_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QAR_H */

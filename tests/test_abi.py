@@ -1,0 +1,92 @@
+"""The C ABI without a GPU: libqar loads, exports every function
+include/qar.h declares, and rejects bad arguments before touching HIP (every
+call below fails validation, so nothing is launched)."""
+import ctypes
+
+import pytest
+
+from block_wise_int8_amd import qar
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qar.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = qar.declared_functions()
+    assert set(names) == set(qar._SIGNATURES), names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.qar_status_string(s)
+    assert L.qar_last_error() == b""
+
+
+A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+B_ = 0x20000
+C = 0x30000
+D = 0x40000
+
+
+def test_quantize_validation(L):
+    q = L.qar_quantize_blocks
+    assert q(None, qar.QAR_BF16, 0, 256, None, None, None) == qar.QAR_OK           # empty call
+    assert q(None, qar.QAR_BF16, 256, 256, B_, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert q(A, qar.QAR_BF16, 256, 100, B_, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert q(A, qar.QAR_BF16, 300, 256, B_, C, None) == qar.QAR_ERR_INVALID_ARG   # n % block
+    assert q(A, 7, 256, 256, B_, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert q(A + 2, qar.QAR_BF16, 256, 256, B_, C, None) == qar.QAR_ERR_MISALIGNED
+    assert q(A, qar.QAR_BF16, 256, 256, B_ + 8, C, None) == qar.QAR_ERR_MISALIGNED
+    assert q(A, qar.QAR_BF16, 256, 256, B_, C + 2, None) == qar.QAR_ERR_MISALIGNED
+    assert q(A, qar.QAR_BF16, 256, 256, A + 256, C, None) == qar.QAR_ERR_INVALID_ARG  # codes overlap x
+    assert q(A, qar.QAR_BF16, (1 << 40) + 256, 256, B_, C, None) == qar.QAR_ERR_INVALID_ARG
+
+
+def _arr(*v):
+    return ctypes.cast((ctypes.c_void_p * len(v))(*v), ctypes.c_void_p)
+
+
+def test_reduce_validation(L):
+    r = L.qar_reduce_quantized
+    codes, scales = _arr(A, B_), _arr(C, D)
+    assert r(None, None, 2, 0, 256, None, None, None, 0, None) == qar.QAR_OK
+    assert r(codes, scales, 0, 256, 256, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    assert r(codes, scales, 33, 256, 256, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    assert r(codes, scales, 2, 256, 64 * 3, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_UNSUPPORTED
+    assert r(_arr(A, B_ + 1), scales, 2, 256, 256, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_MISALIGNED
+    assert r(_arr(A, None), scales, 2, 256, 256, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    # output codes partly overlapping rank 1's codes
+    assert r(codes, scales, 2, 256, 256, B_ + 16, 0x60000, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    # in place on codes but not on scales
+    assert r(codes, scales, 2, 256, 256, B_, 0x60000, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    # optional output with a bad dtype
+    assert r(codes, scales, 2, 256, 256, 0x50000, 0x60000, 0x70000, 9, None) == qar.QAR_ERR_UNSUPPORTED
+
+
+def test_pipelined_validation(L):
+    p = L.qar_reduce_quantized_pipelined
+    codes, scales = _arr(A, B_), _arr(C, D)
+    streams = _arr(0x1234)
+    assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 0, streams, 1, None) == qar.QAR_ERR_INVALID_ARG
+    assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 0, None) == qar.QAR_ERR_INVALID_ARG
+    assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, None, 1, None) == qar.QAR_ERR_INVALID_ARG
+    assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 17, None) == qar.QAR_ERR_INVALID_ARG
+
+
+def test_ring_and_dequantize_validation(L):
+    g = L.qar_ring_step
+    assert g(A, C, B_, qar.QAR_BF16, 0, 256, A, C, None) == qar.QAR_OK
+    assert g(A, C, B_, qar.QAR_BF16, 256, 32, A, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert g(A, C, B_, qar.QAR_BF16, 256, 256, A, D, None) == qar.QAR_ERR_INVALID_ARG   # half in place
+    assert g(A, C, B_, qar.QAR_BF16, 256, 256, B_ + 64, D, None) == qar.QAR_ERR_INVALID_ARG  # codes_out overlaps local
+    assert g(A, C, B_ + 4, qar.QAR_F32, 256, 256, A, C, None) == qar.QAR_ERR_MISALIGNED
+    d = L.qar_dequantize
+    assert d(A, C, 0, 256, None, qar.QAR_F32, None) == qar.QAR_OK
+    assert d(A, C, 512, 256, None, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG
+    assert d(A, C, 512, 256, A + 64, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG    # out overlaps codes
+    assert d(A, C, 512, 256, D, 5, None) == qar.QAR_ERR_UNSUPPORTED
+    assert d(A, C, 500, 256, D, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG

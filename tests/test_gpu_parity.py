@@ -1,0 +1,317 @@
+"""libqar's HIP kernels against the CPU oracle, element by element, through
+the C ABI.  Codes and scales must match bit for bit, dequantized fp32 and
+bf16 values too (the method fixes every rounding; there is no tolerance).
+
+Sizes span several 4096-element tiles plus a ragged tail (n is a multiple
+of the block but not of the tile)."""
+import numpy as np
+import pytest
+import torch
+
+import golden_cases as gc
+from block_wise_int8_amd import qar, synth
+from gpu_util import (assert_same_bits16, assert_same_codes, assert_same_f32, f32_bits, say, to_dev,
+                      to_host)
+
+pytestmark = pytest.mark.gpu
+
+TILE = 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qar.lib()
+    torch.cuda.init()
+
+
+def ragged_n(block: int, tiles: int = 3) -> int:
+    return tiles * TILE + 5 * block
+
+
+def mixed_f32(seed: int, n: int, block: int) -> np.ndarray:
+    """fp32 data with per-block magnitudes across the range plus special
+    blocks: all zero, signed zeros, constant, subnormal, one outlier."""
+    x = synth.wide_range_f32(seed, n, block, log2_span=50)
+    nb = n // block
+    rng = np.random.default_rng(seed + 1)
+    b = rng.permutation(nb)[:6] * block
+    x[b[0]:b[0] + block] = 0.0
+    x[b[1]:b[1] + block] = -0.0
+    x[b[1] + 3] = 1.0
+    x[b[2]:b[2] + block] = np.float32(-3.25)
+    x[b[3]:b[3] + block] = (rng.normal(0, 1, block) * 2.0 ** -140).astype(np.float32)
+    x[b[4]:b[4] + block] = (rng.normal(0, 1, block) * 2.0 ** -149).astype(np.float32)
+    x[b[5] + 7] = np.float32(3.0e38)
+    return x
+
+
+def mixed_bf16(seed: int, n: int, block: int) -> np.ndarray:
+    return synth.f32_to_bf16_bits(mixed_f32(seed, n, block))
+
+
+# ----------------------------------------------------------------------------
+# quantize
+
+
+@pytest.mark.parametrize("block", qar.BLOCK_SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_parity(oracle_lib, dtype, block):
+    n = ragged_n(block)
+    x = mixed_bf16(block, n, block) if dtype == "bf16" else mixed_f32(block, n, block)
+    say(f"quantize {dtype} B={block} n={n}")
+    codes, scales = qar.qar_quantize_blocks(to_dev(x), block)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.quantize(x, block)
+    assert_same_f32(to_host(scales), ws, "scales")
+    assert_same_codes(to_host(codes), wc, "codes")
+
+
+def test_quantize_every_bf16_against_many_scales(oracle_lib):
+    """Every finite bf16 x against 256 absmax values spread over the bf16
+    range: blocks of 256 holding the absmax and 255 values |x| <= absmax."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    h = h[((h >> 7) & 0xFF) != 0xFF]
+    v = (h.astype(np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(77)
+    pos = h[(h > 0) & (h < 0x7F80)]
+    picks = np.concatenate([rng.choice(pos, 248, replace=False),
+                            np.uint16([0x0001, 0x0080, 0x3F80, 0x42FE, 0x7F7F, 0x3C01, 0x4300, 0x0400])])
+    blocks = []
+    for a in picks:
+        av = (np.uint32(a) << 16).view(np.float32)
+        sel = h[np.abs(v) <= av]
+        k = -(-sel.size // 255)
+        sel = np.concatenate([sel, np.zeros(k * 255 - sel.size, np.uint16)]).reshape(k, 255)
+        blocks.append(np.concatenate([np.full((k, 1), a, np.uint16), sel], axis=1))
+    x = np.concatenate(blocks).reshape(-1)
+    say(f"exhaustive bf16 grid n={x.size}")
+    codes, scales = qar.qar_quantize_blocks(to_dev(x), 256)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.quantize(x, 256)
+    assert_same_f32(to_host(scales), ws, "scales")
+    assert_same_codes(to_host(codes), wc, "codes")
+
+
+def test_quantize_f32_near_ties(oracle_lib):
+    """fp32 quotients within a few ulps of every half-integer, for 2048
+    random scales: blocks of 64 = the absmax element + 63 near-tie values."""
+    rng = np.random.default_rng(78)
+    nb = 2048
+    amax = np.exp(rng.uniform(-60, 60, nb)).astype(np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    k = rng.integers(-127, 127, (nb, 63)) + 0.5
+    base = (k * s.astype(np.float64)[:, None]).astype(np.float32)
+    nudge = rng.integers(-3, 4, (nb, 63))
+    x = (base.view(np.int32) + nudge).view(np.float32)
+    x = np.where(np.abs(x) <= amax[:, None], x, base)
+    x = np.concatenate([amax[:, None], x], axis=1).astype(np.float32).reshape(-1)
+    say(f"near ties n={x.size}")
+    codes, scales = qar.qar_quantize_blocks(to_dev(x), 64)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.quantize(x, 64)
+    assert_same_f32(to_host(scales), ws, "scales")
+    assert_same_codes(to_host(codes), wc, "codes")
+
+
+# ----------------------------------------------------------------------------
+# dequantize
+
+
+@pytest.mark.parametrize("block", qar.BLOCK_SIZES)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequantize_parity(oracle_lib, out, block):
+    n = ragged_n(block)
+    rng = np.random.default_rng(block + 3)
+    codes = rng.integers(-128, 128, n).astype(np.int8)
+    scales = np.abs(synth.wide_range_f32(block + 4, n // block, 1, log2_span=110)).astype(np.float32)
+    scales[:6] = np.float32([0.0, 2.0 ** -149, 2.0 ** -140, 1.0 / 127, 2.6e36, 1.0e36])
+    say(f"dequantize {out} B={block} n={n}")
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    y = qar.qar_dequantize(to_dev(codes), to_dev(scales), block, out_dtype=dt)
+    torch.cuda.synchronize()
+    want = oracle_lib.dequantize(codes, scales, block, out)
+    if out == "bf16":
+        assert_same_bits16(to_host(y), want, "bf16 out")
+    else:
+        assert_same_f32(to_host(y), want, "fp32 out")
+
+
+# ----------------------------------------------------------------------------
+# reduce
+
+
+def _rank_codes(oracle_lib, xs, block):
+    qs = [oracle_lib.quantize(x, block) for x in xs]
+    return [q[0] for q in qs], [q[1] for q in qs]
+
+
+@pytest.mark.parametrize("block", qar.BLOCK_SIZES)
+@pytest.mark.parametrize("nranks", [1, 2, 3, 4, 7, 8, 9, 16, 32])
+def test_reduce_parity(oracle_lib, nranks, block):
+    n = ragged_n(block, tiles=2)
+    xs = [mixed_bf16(100 * nranks + r, n, block) for r in range(nranks)]
+    codes, scales = _rank_codes(oracle_lib, xs, block)
+    say(f"reduce N={nranks} B={block} n={n}")
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    out16 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    oc, os_ = qar.qar_reduce_quantized(dc, ds, block, out=out16)
+    out32 = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    oc2, os2 = qar.qar_reduce_quantized(dc, ds, block, out=out32)
+    oc3, os3 = qar.qar_reduce_quantized(dc, ds, block)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce(codes, scales, block)
+    assert_same_f32(to_host(os_), ws, "scales")
+    assert_same_codes(to_host(oc), wc, "codes")
+    assert_same_bits16(to_host(out16), oracle_lib.dequantize(wc, ws, block, "bf16"), "fused bf16 out")
+    assert_same_f32(to_host(out32), oracle_lib.dequantize(wc, ws, block, "f32"), "fused fp32 out")
+    for c, s in ((oc2, os2), (oc3, os3)):
+        assert_same_codes(to_host(c), wc, "codes (other out variant)")
+        assert_same_f32(to_host(s), ws, "scales (other out variant)")
+
+
+def test_reduce_in_place(oracle_lib):
+    block, n, nranks = 256, ragged_n(256), 4
+    xs = [mixed_bf16(900 + r, n, block) for r in range(nranks)]
+    codes, scales = _rank_codes(oracle_lib, xs, block)
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    say("reduce in place into rank 2")
+    qar.qar_reduce_quantized(dc, ds, block, codes_out=dc[2], scales_out=ds[2])
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce(codes, scales, block)
+    assert_same_codes(to_host(dc[2]), wc, "codes")
+    assert_same_f32(to_host(ds[2]), ws, "scales")
+
+
+@pytest.mark.parametrize("nstreams", [1, 4])
+@pytest.mark.parametrize("nchunks", [1, 3, 8, 16, 64])
+def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
+    block, nranks = 64, 5
+    n = ragged_n(block, tiles=6)
+    xs = [mixed_f32(700 + r, n, block) for r in range(nranks)]
+    codes, scales = _rank_codes(oracle_lib, xs, block)
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    out = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    say(f"pipelined nchunks={nchunks} nstreams={nstreams}")
+    oc, os_ = qar.qar_reduce_quantized_pipelined(dc, ds, block, nchunks, streams, out=out)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce(codes, scales, block)
+    assert_same_codes(to_host(oc), wc, "codes")
+    assert_same_f32(to_host(os_), ws, "scales")
+    assert_same_f32(to_host(out), oracle_lib.dequantize(wc, ws, block, "f32"), "out")
+
+
+# ----------------------------------------------------------------------------
+# ring step
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("block", qar.BLOCK_SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ring_step_parity(oracle_lib, dtype, block, in_place):
+    n = ragged_n(block)
+    mk = mixed_bf16 if dtype == "bf16" else mixed_f32
+    x0, x1 = mk(300 + block, n, block), mk(301 + block, n, block)
+    c0, s0 = oracle_lib.quantize(x0, block)
+    dc, ds = to_dev(c0), to_dev(s0)
+    say(f"ring step {dtype} B={block} in_place={in_place}")
+    if in_place:
+        oc, os_ = qar.qar_ring_step(dc, ds, to_dev(x1), block, codes_out=dc, scales_out=ds)
+    else:
+        oc, os_ = qar.qar_ring_step(dc, ds, to_dev(x1), block)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.ring_step(c0, s0, x1, block)
+    assert_same_codes(to_host(oc), wc, "codes")
+    assert_same_f32(to_host(os_), ws, "scales")
+
+
+# ----------------------------------------------------------------------------
+# contract details
+
+
+def test_subrange_call_equals_slice(oracle_lib):
+    """A block-aligned sub-range (offset pointers) is a valid call with the
+    same results in that range."""
+    block, n = 128, ragged_n(128)
+    x = mixed_bf16(55, n, block)
+    dx = to_dev(x)
+    codes, scales = qar.qar_quantize_blocks(dx, block)
+    k0, k1 = 7, n // block - 3
+    sub_c, sub_s = qar.qar_quantize_blocks(dx[k0 * block:k1 * block], block)
+    torch.cuda.synchronize()
+    assert_same_codes(to_host(sub_c), to_host(codes)[k0 * block:k1 * block], "sub-range codes")
+    assert_same_f32(to_host(sub_s), to_host(scales)[k0:k1], "sub-range scales")
+
+
+def test_empty_and_rejected_calls():
+    dx = torch.zeros(512, dtype=torch.bfloat16, device="cuda:0")
+    c, s = qar.qar_quantize_blocks(dx[:0], 256)             # n == 0: nothing enqueued
+    assert c.numel() == 0
+    with pytest.raises(qar.QarError):
+        qar.qar_quantize_blocks(dx[:300], 100)
+    with pytest.raises(qar.QarError):
+        qar.qar_quantize_blocks(dx[1:257], 256)             # 2-byte offset: misaligned
+    codes = torch.zeros(512, dtype=torch.int8, device="cuda:0")
+    scales = torch.zeros(2, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(qar.QarError):
+        qar.qar_reduce_quantized([codes] * 33, [scales] * 33, 256)
+    torch.cuda.synchronize()
+
+
+def test_golden_cases_on_gpu():
+    g = gc.load()
+    B = g["block"]
+    for case in g["quantize"]:
+        x = gc.pad(case["x"], B)
+        for xin in (torch.from_numpy(x).cuda(), torch.from_numpy(x).cuda().to(torch.bfloat16)):
+            codes, scales = qar.qar_quantize_blocks(xin, B)
+            k = len(case["codes"])
+            assert list(to_host(codes)[:k]) == case["codes"], case["name"]
+            want_s = gc.bits_to_f32(case["scale_bits"]) if "scale_bits" in case else np.float32(case["scale"])
+            assert f32_bits(to_host(scales))[0] == f32_bits(want_s)[()], case["name"]
+            y = to_host(qar.qar_dequantize(codes, scales, B, out_dtype=torch.float32))
+            if "dequant" in case:
+                assert np.array_equal(y[:k], np.float32(case["dequant"])), case["name"]
+            for i, h in enumerate(case.get("dequant_bits", [])):
+                if h is not None:
+                    assert f32_bits(y)[i] == int(h, 16), (case["name"], i)
+    for case in g["reduce"]:
+        qs = [qar.qar_quantize_blocks(torch.from_numpy(gc.pad(r, B)).cuda(), B) for r in case["ranks"]]
+        oc, os_ = qar.qar_reduce_quantized([q[0] for q in qs], [q[1] for q in qs], B)
+        assert to_host(os_)[0] == np.float32(case["scale"]), case["name"]
+        assert list(to_host(oc)[:len(case["codes"])]) == case["codes"], case["name"]
+    for case in g["ring_step"]:
+        codes = torch.from_numpy(gc.pad(case["codes_in"], B, np.int8)).cuda()
+        scales = torch.tensor([case["scale_in"]], dtype=torch.float32, device="cuda:0")
+        local = torch.from_numpy(gc.pad(case["local"], B)).cuda().to(torch.bfloat16)
+        oc, os_ = qar.qar_ring_step(codes, scales, local, B)
+        assert to_host(os_)[0] == np.float32(case["scale"]), case["name"]
+        assert list(to_host(oc)[:len(case["codes"])]) == case["codes"], case["name"]
+
+
+def test_beyond_2_pow_31_elements(oracle_lib):
+    """n above 2**31 (64-bit element offsets): quantize and dequantize bf16,
+    checked against the oracle on sampled blocks and the last blocks."""
+    block = 256
+    n = (1 << 31) + 3 * TILE + 7 * block
+    say(f"large n={n}")
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(123)
+    x.normal_(0.0, 1.0, generator=g)
+    codes, scales = qar.qar_quantize_blocks(x, block)
+    y = qar.qar_dequantize(codes, scales, block, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    nb = n // block
+    rng = np.random.default_rng(5)
+    picks = np.concatenate([rng.choice(nb, 2000, replace=False), np.arange(nb - 40, nb)])
+    idx = torch.from_numpy((picks[:, None] * block + np.arange(block)).reshape(-1)).cuda()
+    xs = to_host(x[idx])
+    wc, ws = oracle_lib.quantize(xs, block)
+    assert_same_codes(to_host(codes[idx]), wc, "codes")
+    assert_same_f32(to_host(scales[torch.from_numpy(picks).cuda()]), ws, "scales")
+    assert_same_bits16(to_host(y[idx]), oracle_lib.dequantize(wc, ws, block, "bf16"), "dequantized")
+    del x, codes, scales, y
+    torch.cuda.empty_cache()
