@@ -42,15 +42,17 @@
  *   - Requirements: block is 64, 128 or 256; n % block == 0;
  *     n <= QAR_MAX_ELEMENTS; element and code pointers 16-byte aligned;
  *     scale pointers 4-byte aligned.
- *   - Inputs must be finite.  Output for NaN or infinite input is
- *     unspecified (it is not checked, for speed).
+ *   - Inputs must be finite, and so must every binary32 sum a reduce or
+ *     ring step forms (the sum of finite values can overflow).  Output for
+ *     NaN or infinite input, or for an overflowed sum, is unspecified (it is
+ *     not checked, for speed).
  *   - Output buffers must not overlap input buffers, except where a call
  *     says otherwise.  Partial overlap is rejected with QAR_ERR_INVALID_ARG.
  *   - Any block-aligned sub-range of a valid call (pointers advanced by
  *     k*block elements and k scales) is itself a valid call with the same
  *     results in that range.
- *   - Thread-safe; the only global state is a per-device cache of the
- *     compute-unit count.
+ *   - Thread-safe; the only global state is the per-thread text behind
+ *     qar_last_error().
  */
 #ifndef QAR_H
 #define QAR_H

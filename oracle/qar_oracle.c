@@ -25,7 +25,8 @@
  *          order, separate multiply and add), then quantize(acc)
  *   ring   quantize(fl32(y_in + x_local))
  *   bf16   round-to-nearest-even of the fp32 value to 8 significant bits.
- * Inputs must be finite; the oracle refuses NaN and infinity.
+ * Inputs must be finite; the oracle refuses NaN and infinity, and refuses a
+ * reduce or ring step whose binary32 sum overflows to infinity.
  *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared.
  * x86-64 SSE arithmetic (FLT_EVAL_METHOD == 0): every float operation below
@@ -101,6 +102,17 @@ static void quantize_one_block(const float* v, size_t len, int8_t* q, float* sca
             r = -127.0f;
         q[i] = (int8_t)r;
     }
+}
+
+/* A sum of finite values can still overflow binary32; such a block has no
+ * finite absmax and the method is undefined there, so the oracle refuses it
+ * as it refuses non-finite input. */
+static int all_finite(const float* v, size_t len)
+{
+    for (size_t i = 0; i < len; i++)
+        if (!isfinite(v[i]))
+            return 0;
+    return 1;
 }
 
 static size_t block_count(size_t n, size_t block) { return (n + block - 1) / block; }
@@ -182,6 +194,10 @@ int oracle_reduce(const int8_t* const* codes, const float* const* scales,
         for (size_t r = 1; r < nranks; r++)
             for (size_t i = 0; i < len; i++)
                 acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
         quantize_one_block(acc, len, codes_out + start, scales_out + b);
     }
     free(acc);
@@ -211,6 +227,10 @@ int oracle_ring_step(const int8_t* codes_in, const float* scales_in,
         for (size_t i = 0; i < len; i++)
             acc[i] = dequant_value(codes_in[start + i], scales_in[b]) +
                      load_element(local, dtype, start + i);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
         quantize_one_block(acc, len, codes_out + start, scales_out + b);
     }
     free(acc);

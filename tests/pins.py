@@ -296,6 +296,8 @@ def pin_idempotence(o) -> None:
 
 
 def pin_nonfinite_rejected(o) -> None:
+    """Non-finite input, and a reduce or ring step whose binary32 sum
+    overflows (two values of 3e38), are refused."""
     for bad in (np.inf, -np.inf, np.nan):
         x = np.float32([1.0, bad, 2.0, 3.0])
         try:
@@ -303,6 +305,14 @@ def pin_nonfinite_rejected(o) -> None:
         except ValueError:
             continue
         raise AssertionError("non-finite input accepted")
+    c, s = o.quantize(np.float32([3.0e38, 1.0]), 2)
+    for call in (lambda: o.reduce([c, c], [s, s], 2),
+                 lambda: o.ring_step(c, s, np.float32([3.0e38, 0.0]), 2)):
+        try:
+            call()
+        except ValueError:
+            continue
+        raise AssertionError("overflowing sum accepted")
 
 
 # ----------------------------------------------------------------------------

@@ -30,9 +30,11 @@ def ragged_n(block: int, tiles: int = 3) -> int:
     return tiles * TILE + 5 * block
 
 
-def mixed_f32(seed: int, n: int, block: int) -> np.ndarray:
+def mixed_f32(seed: int, n: int, block: int, outlier: float = 3.0e38) -> np.ndarray:
     """fp32 data with per-block magnitudes across the range plus special
-    blocks: all zero, signed zeros, constant, subnormal, one outlier."""
+    blocks: all zero, signed zeros, constant, subnormal, one outlier.  Data
+    that is summed takes a smaller outlier so that no binary32 sum
+    overflows (the method is undefined for an infinite sum)."""
     x = synth.wide_range_f32(seed, n, block, log2_span=50)
     nb = n // block
     rng = np.random.default_rng(seed + 1)
@@ -43,12 +45,15 @@ def mixed_f32(seed: int, n: int, block: int) -> np.ndarray:
     x[b[2]:b[2] + block] = np.float32(-3.25)
     x[b[3]:b[3] + block] = (rng.normal(0, 1, block) * 2.0 ** -140).astype(np.float32)
     x[b[4]:b[4] + block] = (rng.normal(0, 1, block) * 2.0 ** -149).astype(np.float32)
-    x[b[5] + 7] = np.float32(3.0e38)
+    x[b[5] + 7] = np.float32(outlier)
     return x
 
 
-def mixed_bf16(seed: int, n: int, block: int) -> np.ndarray:
-    return synth.f32_to_bf16_bits(mixed_f32(seed, n, block))
+def mixed_bf16(seed: int, n: int, block: int, outlier: float = 3.0e38) -> np.ndarray:
+    return synth.f32_to_bf16_bits(mixed_f32(seed, n, block, outlier))
+
+
+SUM_OUTLIER = 9.0e36     # 32 of them still sum below the largest binary32
 
 
 # ----------------------------------------------------------------------------
@@ -103,7 +108,7 @@ def test_quantize_f32_near_ties(oracle_lib):
     s = (amax / np.float32(127.0)).astype(np.float32)
     k = rng.integers(-127, 127, (nb, 63)) + 0.5
     base = (k * s.astype(np.float64)[:, None]).astype(np.float32)
-    nudge = rng.integers(-3, 4, (nb, 63))
+    nudge = rng.integers(-3, 4, (nb, 63)).astype(np.int32)
     x = (base.view(np.int32) + nudge).view(np.float32)
     x = np.where(np.abs(x) <= amax[:, None], x, base)
     x = np.concatenate([amax[:, None], x], axis=1).astype(np.float32).reshape(-1)
@@ -151,7 +156,7 @@ def _rank_codes(oracle_lib, xs, block):
 @pytest.mark.parametrize("nranks", [1, 2, 3, 4, 7, 8, 9, 16, 32])
 def test_reduce_parity(oracle_lib, nranks, block):
     n = ragged_n(block, tiles=2)
-    xs = [mixed_bf16(100 * nranks + r, n, block) for r in range(nranks)]
+    xs = [mixed_bf16(100 * nranks + r, n, block, SUM_OUTLIER) for r in range(nranks)]
     codes, scales = _rank_codes(oracle_lib, xs, block)
     say(f"reduce N={nranks} B={block} n={n}")
     dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
@@ -173,7 +178,7 @@ def test_reduce_parity(oracle_lib, nranks, block):
 
 def test_reduce_in_place(oracle_lib):
     block, n, nranks = 256, ragged_n(256), 4
-    xs = [mixed_bf16(900 + r, n, block) for r in range(nranks)]
+    xs = [mixed_bf16(900 + r, n, block, SUM_OUTLIER) for r in range(nranks)]
     codes, scales = _rank_codes(oracle_lib, xs, block)
     dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
     say("reduce in place into rank 2")
@@ -189,7 +194,7 @@ def test_reduce_in_place(oracle_lib):
 def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
     block, nranks = 64, 5
     n = ragged_n(block, tiles=6)
-    xs = [mixed_f32(700 + r, n, block) for r in range(nranks)]
+    xs = [mixed_f32(700 + r, n, block, SUM_OUTLIER) for r in range(nranks)]
     codes, scales = _rank_codes(oracle_lib, xs, block)
     dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
     streams = [torch.cuda.Stream() for _ in range(nstreams)]
@@ -213,7 +218,7 @@ def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
 def test_ring_step_parity(oracle_lib, dtype, block, in_place):
     n = ragged_n(block)
     mk = mixed_bf16 if dtype == "bf16" else mixed_f32
-    x0, x1 = mk(300 + block, n, block), mk(301 + block, n, block)
+    x0, x1 = mk(300 + block, n, block, SUM_OUTLIER), mk(301 + block, n, block, SUM_OUTLIER)
     c0, s0 = oracle_lib.quantize(x0, block)
     dc, ds = to_dev(c0), to_dev(s0)
     say(f"ring step {dtype} B={block} in_place={in_place}")
