@@ -25,16 +25,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
                                                        uint32_t ntiles) {
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
         const bool valid = e0 < n;
+        // Lanes past the end read element 0 instead: blocks never straddle
+        // the end, so their (discarded) results cannot touch a valid block.
+        const size_t ld = valid ? e0 : 0;
         float v[kLaneElems];
-        if (valid) {
-            load16(x + e0, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) v[i] = 0.0f;
-        }
+        load16(x + ld, v);
         const float s = block_max<B>(lane_absmax(v)) / 127.0f;
         const uint4 q = quantize16(v, s);
         if (valid) {
@@ -53,20 +51,19 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, si
                                                      void* __restrict__ out, int out_kind,
                                                      uint32_t ntiles) {
     constexpr int G = 8; // ranks whose loads are in flight together
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
         const bool valid = e0 < n;
-        const size_t blk = e0 / B;
+        const size_t ld = valid ? e0 : 0; // see k_quantize
+        const size_t blk = ld / B;
         float acc[kLaneElems];
         for (int g = 0; g < nranks; g += G) {
             uint4 q[G];
             float s[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                q[j] = make_uint4(0u, 0u, 0u, 0u);
-                s[j] = 0.0f;
-                if (g + j < nranks && valid) {
-                    q[j] = load_b128(rp.codes[g + j] + e0);
+                if (g + j < nranks) {
+                    q[j] = load_b128(rp.codes[g + j] + ld);
                     s[j] = rp.scales[g + j][blk];
                 }
             }
@@ -86,13 +83,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, si
             }
         }
         const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
-        const uint4 qo = quantize16(acc, so);
+        uint32_t w[kLaneElems];
+        const uint4 qo = quantize16(acc, so, w);
         if (valid) {
             store_b128(codes_out + e0, qo);
             if (e0 % B == 0) scales_out[blk] = so;
             if (out_kind != kOutNone) {
                 float y[kLaneElems];
-                dequantize16(qo, so, y);
+                dequantize_words(w, so, y);
                 if (out_kind == kOutBF16)
                     store16(static_cast<uint16_t*>(out) + e0, y);
                 else
@@ -110,22 +108,20 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
                                                         const In* __restrict__ local, size_t n,
                                                         int8_t* codes_out, float* scales_out,
                                                         uint32_t ntiles) {
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
         const bool valid = e0 < n;
-        const size_t blk = e0 / B;
+        const size_t ld = valid ? e0 : 0; // see k_quantize
+        const size_t blk = ld / B;
         float acc[kLaneElems];
-        if (valid) {
-            const uint4 q = load_b128(codes_in + e0);
+        {
+            const uint4 q = load_b128(codes_in + ld);
             const float s = scales_in[blk];
             float x[kLaneElems];
-            load16(local + e0, x);
+            load16(local + ld, x);
             dequantize16(q, s, acc);
 #pragma unroll
             for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + x[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) acc[i] = 0.0f;
         }
         const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
         const uint4 qo = quantize16(acc, so);
@@ -143,7 +139,7 @@ template <int B, typename Out>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restrict__ codes,
                                                          const float* __restrict__ scales, size_t n,
                                                          Out* __restrict__ out, uint32_t ntiles) {
-    for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
         if (e0 >= n) continue;
         const uint4 q = load_b128(codes + e0);
