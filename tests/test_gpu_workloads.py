@@ -1,0 +1,137 @@
+"""Every workload at its full size, through the C ABI, against the CPU
+oracle on every element: quantize each rank, then the one-shot reduce with
+its fused dequantized output (the small-block fp32 workload through the
+4-stream pipelined call, as it is specified), or the N-1 ring steps; plus
+the error bounds against the exact fp64 sum on sampled blocks.
+
+Workloads (seeded, block_wise_int8_amd/synth.py):
+  tiny        N=4  x 4,096 bf16, block 128
+  outliers    N=8  x 16,777,216 bf16, block 256
+  prefill     N=8  x [8192, 5376] bf16, block 256
+  ring        N=4  x [2048, 3840] bf16, block 256 (ring steps)
+  smallblock  N=16 x 67,108,864 fp32, block 64 (16 chunks over 4 streams)
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_wise_int8_amd import qar, synth
+from gpu_util import assert_same_bits16, assert_same_codes, assert_same_f32, say, to_dev, to_host
+from oracle import bounds
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_BLOCKS = 2048
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qar.lib()
+
+
+def _f64(x: np.ndarray) -> np.ndarray:
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def _quantize_all(oracle_lib, w, host):
+    """GPU quantize of every rank, compared with the oracle; returns the
+    device codes/scales and the oracle's."""
+    dc, ds, oc, os_ = [], [], [], []
+    for r, x in enumerate(host):
+        c, s = qar.qar_quantize_blocks(to_dev(x), w.block)
+        torch.cuda.synchronize()
+        wc, ws = oracle_lib.quantize(x, w.block)
+        assert_same_codes(to_host(c), wc, f"{w.key} rank {r} codes")
+        assert_same_f32(to_host(s), ws, f"{w.key} rank {r} scales")
+        dc.append(c), ds.append(s), oc.append(wc), os_.append(ws)
+    say(f"{w.key}: quantize of {w.nranks} ranks bit-exact")
+    return dc, ds, oc, os_
+
+
+def _sample_blocks(w, seed=0):
+    nb = w.n // w.block
+    rng = np.random.default_rng(seed)
+    picks = np.unique(np.concatenate([rng.choice(nb, min(SAMPLE_BLOCKS, nb), replace=False), [0, nb - 1]]))
+    idx = (picks[:, None] * w.block + np.arange(w.block)).reshape(-1)
+    return picks, idx
+
+
+@pytest.mark.parametrize("key", ["tiny", "outliers", "prefill", "smallblock"])
+def test_one_shot_workload(oracle_lib, key):
+    w = synth.WORKLOADS[key]
+    say(f"{key}: generating {w.nranks} x {w.n} {w.dtype}")
+    host = synth.ranks(w)
+    dc, ds, oc, os_ = _quantize_all(oracle_lib, w, host)
+    out_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = torch.empty(w.n, dtype=out_dtype, device="cuda:0")
+    if key == "smallblock":
+        streams = [torch.cuda.Stream() for _ in range(4)]
+        rc, rs = qar.qar_reduce_quantized_pipelined(dc, ds, w.block, 16, streams, out=out)
+    else:
+        rc, rs = qar.qar_reduce_quantized(dc, ds, w.block, out=out)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce(oc, os_, w.block)
+    assert_same_codes(to_host(rc), wc, f"{key} reduce codes")
+    assert_same_f32(to_host(rs), ws, f"{key} reduce scales")
+    kind = "bf16" if w.dtype == "bf16" else "f32"
+    want_out = oracle_lib.dequantize(wc, ws, w.block, kind)
+    got_out = to_host(out)
+    if kind == "bf16":
+        assert_same_bits16(got_out, want_out, f"{key} fused dequantize")
+    else:
+        assert_same_f32(got_out, want_out, f"{key} fused dequantize")
+    say(f"{key}: reduce + fused dequantize bit-exact")
+
+    # error against the exact sum on sampled blocks
+    picks, idx = _sample_blocks(w)
+    xs = [_f64(x[idx]) for x in host]
+    exact = np.sum(xs, axis=0)
+    ys = [oracle_lib.dequantize(c[idx], s[picks], w.block, "f32") for c, s in zip(oc, os_)]
+    deq = oracle_lib.dequantize(wc[idx], ws[picks], w.block, "f32").astype(np.float64)
+    err = np.abs(deq - exact)
+    rig = bounds.oneshot_bound(xs, [s[picks] for s in os_], ys, ws[picks], w.block)
+    simple = bounds.oneshot_bound_simple([s[picks] for s in os_], ws[picks], exact, w.block)
+    assert np.all(err <= rig), f"{key}: rigorous bound violated, worst ratio {np.max(err / rig)}"
+    assert np.all(err <= simple), f"{key}: N*max_scale/2 + 1e-6|sum| violated, worst {np.max(err / simple)}"
+    say(f"{key}: max |err|/bound rigorous {np.max(err / rig):.3f}, simple {np.max(err / simple):.3f}")
+    if kind == "bf16":
+        out64 = _f64(want_out[idx])
+        assert np.all(np.abs(out64 - exact) <= rig + 2.0 ** -8 * np.abs(out64))
+
+
+def test_ring_workload(oracle_lib):
+    """quantize(x_0), then N-1 ring steps adding x_1 .. x_{N-1}; every step
+    bit-exact, and within the ring bound of the exact partial sum."""
+    w = synth.WORKLOADS["ring"]
+    host = synth.ranks(w)
+    B = w.block
+    c, s = qar.qar_quantize_blocks(to_dev(host[0]), B)
+    wc, ws = oracle_lib.quantize(host[0], B)
+    torch.cuda.synchronize()
+    assert_same_codes(to_host(c), wc, "ring step 0 codes")
+    picks, idx = _sample_blocks(w, 1)
+    exact = _f64(host[0][idx])
+    step_scales, step_values = [ws[picks]], [exact.copy()]
+    for k in range(1, w.nranks):
+        p = (oracle_lib.dequantize(wc[idx], ws[picks], B, "f32") + _f64(host[k][idx]).astype(np.float32))
+        c, s = qar.qar_ring_step(c, s, to_dev(host[k]), B, codes_out=c, scales_out=s)     # in place
+        torch.cuda.synchronize()
+        wc, ws = oracle_lib.ring_step(wc, ws, host[k], B)
+        assert_same_codes(to_host(c), wc, f"ring step {k} codes")
+        assert_same_f32(to_host(s), ws, f"ring step {k} scales")
+        exact = exact + _f64(host[k][idx])
+        step_scales.append(ws[picks])
+        step_values.append(p.astype(np.float32))
+        deq = oracle_lib.dequantize(wc[idx], ws[picks], B, "f32").astype(np.float64)
+        err = np.abs(deq - exact)
+        rig = bounds.ring_bound(step_scales, step_values, B)
+        simple = bounds.ring_bound_simple(step_scales, exact, B)
+        assert np.all(err <= rig), f"ring step {k}: bound violated, worst {np.max(err / rig)}"
+        # sum_j s_j/2 + 1e-6|sum| drops the fp32 rounding of each step's
+        # add and quotient; it is reported, the rigorous bound decides
+        say(f"ring step {k}: bit-exact; max err {err.max():.4g}, err/bound {np.max(err / rig):.4f}, "
+            f"err/(sum s_j/2 + 1e-6|sum|) {np.max(err / simple):.4f}")
