@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--cpu-reps", type=int, default=4, help="oracle repetitions for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the reduce-only and ring-step lines")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="only run 8 device-to-device copies of this many MiB (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -94,6 +96,18 @@ def main() -> int:
         return 1
     qar.lib()
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of these
+        # dispatches calibrate the counters (bytes read = bytes written =
+        # copy size)
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": nbytes, "launches": 8}))
+        return 0
     w = synth.WORKLOADS[args.workload]
     N, n, B = w.nranks, w.n, w.block
     nb = n // B
