@@ -52,10 +52,11 @@ class Oracle:
         lib.oracle_dequantize_bf16.argtypes = [vp, vp, sz, sz, vp]
         lib.oracle_reduce.argtypes = [vp, vp, sz, sz, sz, vp, vp]
         lib.oracle_ring_step.argtypes = [vp, vp, vp, ctypes.c_int, sz, sz, vp, vp]
+        lib.oracle_reduce_unquantized.argtypes = [vp, ctypes.c_int, sz, sz, vp]
         lib.oracle_f32_to_bf16.argtypes = [vp, sz, vp]
         lib.oracle_f32_to_bf16.restype = None
         for name in ("oracle_quantize", "oracle_dequantize_f32", "oracle_dequantize_bf16",
-                     "oracle_reduce", "oracle_ring_step"):
+                     "oracle_reduce", "oracle_ring_step", "oracle_reduce_unquantized"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
 
@@ -152,6 +153,23 @@ class Oracle:
                                        self._ptr(out_c), self._ptr(out_s))
         self._check(rc, "ring_step")
         return out_c, out_s
+
+    def reduce_unquantized(self, xs: list) -> np.ndarray:
+        """Rank-order fp32 sum of N unquantized buffers, in their own dtype."""
+        xs = [np.ascontiguousarray(x).reshape(-1) for x in xs]
+        if not xs:
+            raise ValueError("need at least one rank")
+        dt = self._dtype_of(xs[0])
+        n = xs[0].size
+        for x in xs:
+            if x.size != n or self._dtype_of(x) != dt:
+                raise ValueError("rank buffers differ in size or type")
+        ptrs = (ctypes.c_void_p * len(xs))(*[self._ptr(x) for x in xs])
+        out = np.empty(n, xs[0].dtype)
+        rc = self.lib.oracle_reduce_unquantized(ctypes.cast(ptrs, ctypes.c_void_p), dt, len(xs), n,
+                                                self._ptr(out))
+        self._check(rc, "reduce_unquantized")
+        return out
 
     def f32_to_bf16(self, x: np.ndarray) -> np.ndarray:
         x = np.ascontiguousarray(x, np.float32).reshape(-1)

@@ -51,6 +51,36 @@ def rn32(x: Fraction) -> Fraction:
     return sign * r
 
 
+def rn_bf16(x: Fraction) -> Fraction:
+    """Round an exact rational to the nearest bfloat16 value (8-bit
+    significand, binary32 exponent range), ties to even."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while _TWO ** e > a:
+        e -= 1
+    while _TWO ** (e + 1) <= a:
+        e += 1
+    e = max(e, _EMIN)
+    quantum = _TWO ** (e - 7)
+    m = a / quantum
+    whole = m.numerator // m.denominator
+    frac = m - whole
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and whole % 2 == 1):
+        whole += 1
+    return sign * whole * quantum
+
+
+def reduce_unquantized(ranks: list[list[Fraction]], to_bf16: bool) -> list[Fraction]:
+    """Rank-order binary32 sum of exact values, then bf16 rounding if asked."""
+    acc = list(ranks[0])
+    for r in ranks[1:]:
+        acc = [rn32(a + b) for a, b in zip(acc, r)]
+    return [rn_bf16(a) for a in acc] if to_bf16 else acc
+
+
 def to_fraction(v) -> Fraction:
     """Exact value of a Python/numpy float (binary32 or binary64)."""
     return Fraction(float(v))

@@ -462,6 +462,32 @@ def pin_ring_bound(o) -> None:
         assert np.all(err <= bounds.ring_bound_simple(step_scales, exact, w.block)), f"simple ring bound step {k}"
 
 
+# ----------------------------------------------------------------------------
+# unquantized comparator
+
+
+def pin_reduce_unquantized(o) -> None:
+    """The unquantized reduce equals the exact-rational brute force (rank
+    order, one binary32 rounding per add, bf16 rounding of the sum), keeps
+    rank order ((1 + 1) + 2**25 vs 2**25 + 1 + 1), and sums integers
+    exactly."""
+    rng = np.random.default_rng(29)
+    for nr, kind in ((1, "bf16"), (2, "f32"), (3, "bf16"), (5, "f32"), (8, "bf16")):
+        v = (rng.normal(0, 1, (nr, 40)) * np.exp(rng.normal(0, 4, (nr, 40)))).astype(np.float32)
+        xs = [synth.f32_to_bf16_bits(r) if kind == "bf16" else r for r in v]
+        got = o.reduce_unquantized(xs)
+        fr = [[brute.bf16_bits_to_fraction(h) for h in x] if kind == "bf16" else [Fraction(float(t)) for t in x]
+              for x in xs]
+        want = brute.reduce_unquantized(fr, kind == "bf16")
+        got_fr = [brute.bf16_bits_to_fraction(h) for h in got] if kind == "bf16" else [Fraction(float(t)) for t in got]
+        assert got_fr == want, f"unquantized reduce differs from brute force (N={nr}, {kind})"
+    big = np.float32([1.0, 1.0, 2.0 ** 25])
+    xs = [np.float32([b]) for b in big]
+    assert o.reduce_unquantized(xs)[0] == np.float32(2.0 ** 25 + 2.0), "rank order"
+    ints = [np.arange(-50, 50, dtype=np.float32) * (r + 1) for r in range(6)]
+    assert np.array_equal(o.reduce_unquantized(ints), np.arange(-50, 50, dtype=np.float32) * 21)
+
+
 ALL_PINS = [
     pin_scale_closed_form,
     pin_zero_and_signed_zero,
@@ -470,6 +496,7 @@ ALL_PINS = [
     pin_reduce_brute_tiny,
     pin_reduce_rank_order,
     pin_ring_brute_tiny,
+    pin_reduce_unquantized,
     pin_dequant_exact,
     pin_bf16_rounding,
     pin_block_layout,

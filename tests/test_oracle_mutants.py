@@ -20,7 +20,8 @@ MUTANTS = {
                  ""),
     "zero_rule_on_absmax": ("if (s == 0.0f) {", "if (absmax == 0.0f) {"),
     "absmax_without_abs": ("float m = fabsf(v[i]);", "float m = v[i];"),
-    "reduce_drops_last_rank": ("for (size_t r = 1; r < nranks; r++)", "for (size_t r = 1; r + 1 < nranks; r++)"),
+    "reduce_drops_last_rank": ("for (size_t r = 1; r < nranks; r++)\n            for (size_t i = 0; i < len; i++)",
+                               "for (size_t r = 1; r + 1 < nranks; r++)\n            for (size_t i = 0; i < len; i++)"),
     "reduce_rank_order": ("acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);",
                           "acc[i] = acc[i] + dequant_value(codes[nranks - r][start + i], scales[nranks - r][b]);"),
     "reduce_fma": ("acc[i] = acc[i] + dequant_value(codes[r][start + i], scales[r][b]);",
@@ -33,6 +34,10 @@ MUTANTS = {
     "ring_local_as_bf16": ("load_element(local, dtype, start + i);", "load_element(local, ORACLE_BF16, start + i);"),
     "bf16_ties_away": ("if (rest > 0x8000u || (rest == 0x8000u && (upper & 1u)))", "if (rest >= 0x8000u)"),
     "bf16_truncates": ("upper += 1u;", "upper += 0u;"),
+    "unquantized_drops_rank": ("for (size_t r = 1; r < nranks; r++)\n            acc = acc + load_element(x[r], dtype, i);",
+                               "for (size_t r = 2; r < nranks; r++)\n            acc = acc + load_element(x[r], dtype, i);"),
+    "unquantized_reverse_order": ("float acc = load_element(x[0], dtype, i);\n        for (size_t r = 1; r < nranks; r++)\n            acc = acc + load_element(x[r], dtype, i);",
+                                  "float acc = load_element(x[nranks - 1], dtype, i);\n        for (size_t r = 1; r < nranks; r++)\n            acc = acc + load_element(x[nranks - 1 - r], dtype, i);"),
 }
 
 
