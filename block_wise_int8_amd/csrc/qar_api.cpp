@@ -236,4 +236,26 @@ qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, ui
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_dequantize");
 }
 
+qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t n, qar_dtype dtype, void* out,
+                                  void* stream) {
+    if (n == 0) return QAR_OK;
+    if (!x || !out || nranks == 0 || nranks > QAR_MAX_RANKS) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (n % 16 != 0 || n > QAR_MAX_ELEMENTS) return QAR_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return QAR_ERR_MISALIGNED;
+    const size_t bytes = n * dtype_bytes(dtype);
+    const Range oo = range(out, bytes);
+    qar::PlainPtrs xp;
+    memset(&xp, 0, sizeof xp);
+    for (uint32_t r = 0; r < nranks; ++r) {
+        if (!x[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(x[r], 16)) return QAR_ERR_MISALIGNED;
+        if (bad_overlap(oo, range(x[r], bytes), true)) return QAR_ERR_INVALID_ARG;
+        xp.x[r] = x[r];
+    }
+    const hipError_t e = qar::launch_reduce_unquantized(xp, (int)nranks, n, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32,
+                                                        out, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_unquantized");
+}
+
 } // extern "C"

@@ -151,6 +151,82 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// the unquantized comparator: fp32 rank-order sum of N bf16/fp32 buffers
+
+template <typename T>
+struct RawVec; // one lane's 16 elements as 16-byte words
+template <>
+struct RawVec<uint16_t> {
+    static constexpr int kWords = 2;
+    static constexpr int kGroup = 8; // ranks in flight together
+};
+template <>
+struct RawVec<float> {
+    static constexpr int kWords = 4;
+    static constexpr int kGroup = 4;
+};
+
+template <typename T>
+__device__ __forceinline__ void widen(const uint4 (&raw)[RawVec<T>::kWords], float (&v)[kLaneElems]);
+
+template <>
+__device__ __forceinline__ void widen<uint16_t>(const uint4 (&raw)[2], float (&v)[kLaneElems]) {
+    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[2 * j] = bf16_lo(w[j]);
+        v[2 * j + 1] = bf16_hi(w[j]);
+    }
+}
+
+template <>
+__device__ __forceinline__ void widen<float>(const uint4 (&raw)[4], float (&v)[kLaneElems]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[4 * j + 0] = __builtin_bit_cast(float, raw[j].x);
+        v[4 * j + 1] = __builtin_bit_cast(float, raw[j].y);
+        v[4 * j + 2] = __builtin_bit_cast(float, raw[j].z);
+        v[4 * j + 3] = __builtin_bit_cast(float, raw[j].w);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_reduce_unquantized(PlainPtrs xp, int nranks, size_t n, T* out,
+                                                                 uint32_t ntiles) {
+    constexpr int W = RawVec<T>::kWords, G = RawVec<T>::kGroup;
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
+        const bool valid = e0 < n;
+        const size_t ld = valid ? e0 : 0; // see k_quantize
+        float acc[kLaneElems];
+        for (int g = 0; g < nranks; g += G) {
+            uint4 raw[G][W];
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (g + j < nranks)
+#pragma unroll
+                    for (int k = 0; k < W; ++k)
+                        raw[j][k] = load_b128(static_cast<const T*>(xp.x[g + j]) + ld + k * (kLaneElems / W));
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (g + j < nranks) {
+                    float v[kLaneElems];
+                    widen<T>(raw[j], v);
+                    if (g + j == 0) {
+#pragma unroll
+                        for (int i = 0; i < kLaneElems; ++i) acc[i] = v[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + v[i];
+                    }
+                }
+            }
+        }
+        if (valid) store16(out + e0, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 namespace {
@@ -219,6 +295,18 @@ hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void
 }
 
 } // namespace
+
+hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
+                                     hipStream_t st) {
+    const Grid g = grid_for(n);
+    if (kind == kInBF16)
+        hipLaunchKernelGGL((k_reduce_unquantized<uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, xp, nranks, n,
+                           static_cast<uint16_t*>(out), g.ntiles);
+    else
+        hipLaunchKernelGGL((k_reduce_unquantized<float>), dim3(g.blocks), dim3(kThreads), 0, st, xp, nranks, n,
+                           static_cast<float*>(out), g.ntiles);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
                            hipStream_t st) {

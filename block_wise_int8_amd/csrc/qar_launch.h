@@ -20,6 +20,12 @@ struct RankPtrs {
     const float* scales[kMaxRanks];
 };
 
+struct PlainPtrs {
+    const void* x[kMaxRanks];
+};
+
+hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
+                                     hipStream_t st);
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
                            hipStream_t st);
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,

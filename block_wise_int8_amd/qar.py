@@ -31,6 +31,7 @@ _SIGNATURES = {
     "qar_reduce_quantized_pipelined": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _u32, _vp, _u32, _vp],
     "qar_ring_step": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
+    "qar_reduce_unquantized": [_vp, _u32, _sz, _int, _vp, _vp],
     "qar_status_string": [_int],
     "qar_last_error": [],
 }
@@ -206,4 +207,19 @@ def qar_dequantize(codes: torch.Tensor, scales: torch.Tensor, block: int, out: t
         out = torch.empty(n, dtype=out_dtype, device=codes.device)
     _check(lib().qar_dequantize(codes.data_ptr(), scales.data_ptr(), n, block, _dev(out, "out").data_ptr(),
                                 _dtype_code(out.dtype), _stream(stream)), "qar_dequantize")
+    return out
+
+
+def qar_reduce_unquantized(xs: list[torch.Tensor], out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The unquantized comparator: rank-order fp32 sum of N bf16/fp32 buffers."""
+    if not xs:
+        raise ValueError("need at least one rank")
+    for x in xs:
+        _dev(x, "x[r]")
+    n = xs[0].numel()
+    if out is None:
+        out = torch.empty(n, dtype=xs[0].dtype, device=xs[0].device)
+    ptrs = _ptrs(xs)
+    _check(lib().qar_reduce_unquantized(ctypes.cast(ptrs, _vp), len(xs), n, _dtype_code(xs[0].dtype),
+                                        _dev(out, "out").data_ptr(), _stream(stream)), "qar_reduce_unquantized")
     return out

@@ -39,7 +39,8 @@
  *     returns QAR_ERR_HIP; qar_last_error() then names the HIP error.
  *   - n == 0 is a valid empty call: QAR_OK, nothing enqueued, no pointer is
  *     read.
- *   - Requirements: block is 64, 128 or 256; n % block == 0;
+ *   - Requirements (calls with a block argument): block is 64, 128 or 256;
+ *     n % block == 0;
  *     n <= QAR_MAX_ELEMENTS; element and code pointers 16-byte aligned;
  *     scale pointers 4-byte aligned.
  *   - Inputs must be finite, and so must every binary32 sum a reduce or
@@ -156,6 +157,20 @@ qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in,
  */
 qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, uint32_t block,
                           void* out, qar_dtype out_dtype, void* stream);
+
+/*
+ * The comparator the pages measure against: the same N-way reduction on the
+ * unquantized data (EQuARX abstract: the 1.8x is over a BF16 AllReduce).
+ * For each element the binary32 sum of the ranks' values in rank order,
+ * stored in the input type (bf16: rounded to nearest even).
+ *   x       [in]  HOST array of nranks DEVICE pointers, each n elements of
+ *                 dtype, rank order.
+ *   nranks  1 .. QAR_MAX_RANKS.
+ *   n       any multiple of 16 (no block structure).
+ *   out     [out] n elements of dtype; may be exactly one input buffer.
+ */
+qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t n, qar_dtype dtype,
+                                  void* out, void* stream);
 
 /* Static text for a status code. */
 const char* qar_status_string(qar_status status);

@@ -90,3 +90,17 @@ def test_ring_and_dequantize_validation(L):
     assert d(A, C, 512, 256, A + 64, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG    # out overlaps codes
     assert d(A, C, 512, 256, D, 5, None) == qar.QAR_ERR_UNSUPPORTED
     assert d(A, C, 500, 256, D, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG
+
+
+def test_unquantized_validation(L):
+    u = L.qar_reduce_unquantized
+    xs = _arr(A, B_)
+    assert u(None, 2, 0, qar.QAR_BF16, None, None) == qar.QAR_OK
+    assert u(xs, 0, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert u(xs, 33, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert u(xs, 2, 250, qar.QAR_BF16, C, None) == qar.QAR_ERR_INVALID_ARG       # n % 16
+    assert u(xs, 2, 256, 4, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert u(xs, 2, 256, qar.QAR_BF16, C + 8, None) == qar.QAR_ERR_MISALIGNED
+    assert u(_arr(A, B_ + 2), 2, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_MISALIGNED
+    assert u(_arr(A, None), 2, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert u(xs, 2, 256, qar.QAR_BF16, A + 32, None) == qar.QAR_ERR_INVALID_ARG    # partial overlap

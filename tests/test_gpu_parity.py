@@ -233,6 +233,30 @@ def test_ring_step_parity(oracle_lib, dtype, block, in_place):
 
 
 # ----------------------------------------------------------------------------
+# the unquantized comparator
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nranks", [1, 2, 5, 8, 9, 16, 32])
+def test_reduce_unquantized_parity(oracle_lib, nranks, dtype):
+    n = 2 * TILE + 16 * 7
+    mk = mixed_bf16 if dtype == "bf16" else mixed_f32
+    xs = [mk(500 + nranks * 40 + r, n, 16, SUM_OUTLIER) for r in range(nranks)]
+    say(f"unquantized reduce N={nranks} {dtype} n={n}")
+    dx = [to_dev(x) for x in xs]
+    out = qar.qar_reduce_unquantized(dx)
+    qar.qar_reduce_unquantized(dx, out=dx[-1])                # in place into the last rank
+    torch.cuda.synchronize()
+    want = oracle_lib.reduce_unquantized(xs)
+    if dtype == "bf16":
+        assert_same_bits16(to_host(out), want, "sum")
+        assert_same_bits16(to_host(dx[-1]), want, "sum in place")
+    else:
+        assert_same_f32(to_host(out), want, "sum")
+        assert_same_f32(to_host(dx[-1]), want, "sum in place")
+
+
+# ----------------------------------------------------------------------------
 # contract details
 
 
