@@ -261,7 +261,12 @@ def main() -> int:
 
     if not args.no_extras:
         result["reduce_only"] = reduce_only(args, qar, torch, sets, B, N, n, qbytes)
+        result["dequantize"] = dequantize_bench(qar, torch, sets, B, n, qbytes)
+        result["unquantized_comparator"] = comparator_bench(qar, torch, synth, w, dev, args.skew,
+                                                            result["reduce_only"]["avg_us"], r_us, q_us)
         result["ring_step"] = ring_bench(qar, torch, np, synth, dev)
+        result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
+        result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, w, host, sets[0], torch)
@@ -293,6 +298,156 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "payload_GBps": round(N * n * 2 / (us * 1e-6) / 1e9, 1),
             "note": "back-to-back launches over rotated buffer sets, out=NULL"}
+
+
+def _loop_us(torch, fn, count, reps, warmup=3):
+    """Average time of fn(i) over reps back-to-back launches (i cycles over
+    `count` buffer sets), one HIP event pair."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i % count)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(reps):
+        fn(i % count)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e3
+
+
+def _rate(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def _rank_block(torch, tensors, skew, dev):
+    """Copy N equal 1-D tensors into one allocation at a stride of
+    (bytes + skew); returns views."""
+    nbytes = tensors[0].numel() * tensors[0].element_size()
+    stride = nbytes + skew
+    big = torch.empty(len(tensors) * stride, dtype=torch.uint8, device=dev)
+    views = []
+    for r, t in enumerate(tensors):
+        v = big[r * stride:r * stride + nbytes].view(t.dtype)
+        v.copy_(t)
+        views.append(v)
+    return views
+
+
+def dequantize_bench(qar, torch, sets, B, n, qbytes):
+    """qar_dequantize of a reduce output to bf16: reads qbytes, writes 2n."""
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=sets[0]["out"].device) for _ in range(len(sets))]
+
+    def fn(i):
+        st = sets[i]
+        qar.qar_dequantize(st["codes_out"], st["scales_out"], B, out=outs[i])
+    return _rate(qbytes + 2 * n, _loop_us(torch, fn, len(sets), 100))
+
+
+def comparator_bench(qar, torch, synth, w, dev, skew, reduce_only_us, reduce_out_us, quant_us):
+    """The unquantized N-way bf16 reduce (rank-order fp32 sum, bf16 out) on
+    the same shape: reads N*2n, writes 2n.  Ratios to the quantized path
+    are the one-GPU analog of the pages' speed-up over a BF16 AllReduce."""
+    N, n = w.nranks, w.n
+    ranks = [synth.device_rank(w, r, dev) for r in range(N)]
+    nsets = 4                                   # 4 x 302 MB > 1 GiB
+    sets = []
+    for _ in range(nsets):
+        sets.append((_rank_block(torch, ranks, skew, dev), torch.empty(n, dtype=torch.bfloat16, device=dev)))
+    del ranks
+
+    def fn(i):
+        xs, out = sets[i]
+        qar.qar_reduce_unquantized(xs, out=out)
+    us = _loop_us(torch, fn, nsets, 50)
+    res = _rate(N * n * 2 + n * 2, us)
+    res["speedup_of_quantized_reduce"] = round(us / reduce_only_us, 3)
+    res["speedup_of_quantized_step"] = round(us / (quant_us + reduce_out_us), 3)
+    res["note"] = ("speedup_of_quantized_reduce = this time / fused quantized reduce time (same N, n); "
+                   "speedup_of_quantized_step = this time / (quantize own + fused reduce with bf16 out)")
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_bench(qar, torch, synth, dev, skew):
+    """Fused reduce with bf16 out on the prefill-shaped workload
+    (N=8 x [8192, 5376] bf16, block 256), data drawn on the GPU."""
+    w = synth.WORKLOADS["prefill"]
+    N, n, B = w.nranks, w.n, w.block
+    nb = n // B
+    codes, scales = [], []
+    for r in range(N):
+        c, s = qar.qar_quantize_blocks(synth.device_rank(w, r, dev), B)
+        codes.append(c), scales.append(s)
+    nsets = 3                                   # 3 x 490 MB
+    sets = []
+    for _ in range(nsets):
+        sets.append((_rank_block(torch, codes, skew, dev), [s.clone() for s in scales],
+                     torch.empty(n, dtype=torch.int8, device=dev), torch.empty(nb, dtype=torch.float32, device=dev),
+                     torch.empty(n, dtype=torch.bfloat16, device=dev)))
+    del codes
+
+    def fn(i):
+        c, s, co, so, out = sets[i]
+        qar.qar_reduce_quantized(c, s, B, co, so, out=out)
+    qbytes = n + 4 * nb
+    res = _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fn, nsets, 50))
+    res["workload"] = w.description + ", fused bf16 out"
+
+    def fn2(i):
+        c, s, co, so, out = sets[i]
+        qar.qar_reduce_quantized(c, s, B, co, so)
+    res["reduce_only"] = _rate((N + 1) * qbytes, _loop_us(torch, fn2, nsets, 50))
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def pipelined_bench(qar, torch, synth, dev, skew):
+    """Small-block fp32 workload (N=16 x 67,108,864, block 64): the fused
+    reduce (no out) as one launch and cut into chunks over streams (the
+    pipeline-depth sweep).  Results are bit-identical for every setting."""
+    w = synth.WORKLOADS["smallblock"]
+    N, n, B = w.nranks, w.n, w.block
+    nb = n // B
+    codes, scales = [], []
+    for r in range(N):
+        c, s = qar.qar_quantize_blocks(synth.device_rank(w, r, dev), B)
+        codes.append(c), scales.append(s)
+    nsets = 2                                   # 2 x 1.2 GB
+    sets = []
+    for _ in range(nsets):
+        sets.append((_rank_block(torch, codes, skew, dev), [s.clone() for s in scales],
+                     torch.empty(n, dtype=torch.int8, device=dev), torch.empty(nb, dtype=torch.float32, device=dev)))
+    del codes
+    qbytes = n + 4 * nb
+    nbytes = (N + 1) * qbytes
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    sweep = []
+
+    def one(i):
+        c, s, co, so = sets[i]
+        qar.qar_reduce_quantized(c, s, B, co, so)
+    r = _rate(nbytes, _loop_us(torch, one, nsets, 20))
+    r.update({"nchunks": 1, "nstreams": 0, "call": "qar_reduce_quantized"})
+    sweep.append(r)
+    for nchunks, nstr in ((1, 1), (4, 4), (16, 4), (64, 4), (16, 1)):
+        def fn(i, nchunks=nchunks, nstr=nstr):
+            c, s, co, so = sets[i]
+            qar.qar_reduce_quantized_pipelined(c, s, B, nchunks, streams[:nstr], co, so)
+        # the HIP runtime's first cross-stream event waits stall the host
+        # for milliseconds; a long warm-up measures the steady state
+        r = _rate(nbytes, _loop_us(torch, fn, nsets, 20, warmup=30))
+        r.update({"nchunks": nchunks, "nstreams": nstr, "call": "qar_reduce_quantized_pipelined"})
+        sweep.append(r)
+    del sets
+    torch.cuda.empty_cache()
+    best = min(sweep, key=lambda x: x["avg_us"])
+    return {"workload": w.description + ", reduce without out", "sweep": sweep,
+            "best": {k: best[k] for k in ("nchunks", "nstreams", "avg_us", "GBps", "hbm_frac")}}
 
 
 def ring_bench(qar, torch, np, synth, dev):

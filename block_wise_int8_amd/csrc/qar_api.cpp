@@ -94,6 +94,37 @@ void fill_ranks(qar::RankPtrs& rp, const int8_t* const* codes, const float* cons
     }
 }
 
+// The pipelined call's events, created once per thread and device and then
+// reused.  Re-recording an event does not disturb waits already enqueued on
+// its previous record, so consecutive calls may share them.  They are never
+// destroyed (a handful per thread and device, released with the process).
+constexpr int kEventDevices = 64;
+struct EventSet {
+    bool made;
+    hipEvent_t ev[1 + QAR_MAX_STREAMS];
+};
+thread_local EventSet g_events[kEventDevices];
+
+hipError_t pipeline_events(hipEvent_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kEventDevices) return hipErrorInvalidDevice;
+    EventSet& set = g_events[dev];
+    if (!set.made) {
+        for (int i = 0; i < 1 + QAR_MAX_STREAMS; ++i) {
+            e = hipEventCreateWithFlags(&set.ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(set.ev[j]);
+                return e;
+            }
+        }
+        set.made = true;
+    }
+    *out = set.ev;
+    return hipSuccess;
+}
+
 int out_kind(const void* out, qar_dtype d) {
     if (!out) return qar::kOutNone;
     return d == QAR_BF16 ? qar::kOutBF16 : qar::kOutF32;
@@ -165,17 +196,12 @@ qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const floa
     const size_t out_bytes = out ? (out_dtype == QAR_BF16 ? 2 : 4) : 0;
     const uint32_t used = (uint32_t)(chunks < nstreams ? chunks : nstreams);
 
-    hipEvent_t start, done[QAR_MAX_STREAMS];
-    hipError_t e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-    uint32_t made = 0;
-    for (; made < used; ++made) {
-        e = hipEventCreateWithFlags(&done[made], hipEventDisableTiming);
-        if (e != hipSuccess) break;
-    }
-    if (e == hipSuccess) e = hipEventRecord(start, main_st);
+    hipEvent_t* ev = nullptr; // ev[0]: start, ev[1 + i]: stream i done
+    hipError_t e = pipeline_events(&ev);
+    if (e != hipSuccess) return hip_fail(e, "qar_reduce_quantized_pipelined: events");
+    e = hipEventRecord(ev[0], main_st);
     for (uint32_t i = 0; e == hipSuccess && i < used; ++i)
-        e = hipStreamWaitEvent((hipStream_t)streams[i], start, 0);
+        e = hipStreamWaitEvent((hipStream_t)streams[i], ev[0], 0);
     for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
         const size_t b0 = c * per;
         if (b0 >= nb) break;
@@ -188,12 +214,9 @@ qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const floa
                                out_c, kind, (hipStream_t)streams[c % used]);
     }
     for (uint32_t i = 0; e == hipSuccess && i < used; ++i) {
-        e = hipEventRecord(done[i], (hipStream_t)streams[i]);
-        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, done[i], 0);
+        e = hipEventRecord(ev[1 + i], (hipStream_t)streams[i]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, ev[1 + i], 0);
     }
-    // Events may be destroyed while pending; HIP releases them on completion.
-    (void)hipEventDestroy(start);
-    for (uint32_t i = 0; i < made; ++i) (void)hipEventDestroy(done[i]);
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_pipelined");
 }
 

@@ -157,3 +157,37 @@ def wide_range_f32(seed: int, n: int, block: int, log2_span: int = 60) -> np.nda
     e = rng.integers(-log2_span, log2_span + 1, nb)
     v *= np.repeat(np.ldexp(1.0, e), block)[:n]
     return v.astype(np.float32)
+
+
+def device_rank(w: Workload, r: int, device, seed_offset: int = 0):
+    """The same recipe drawn on the GPU with torch's generator (seeded with
+    w.seed * 1000 + r): a different random stream from the host recipe, for
+    throughput runs that need no CPU comparison.  Returns a 1-D torch tensor
+    (bfloat16 or float32)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000 + r + seed_offset)
+    n = w.n
+    if w.key in ("tiny", "outliers"):
+        v = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        if w.key == "outliers":
+            k = n // 1000
+            pos = torch.randperm(n, generator=g, device=device)[:k]
+            v[pos] = torch.randn(k, generator=g, device=device) * 50.0
+    elif w.key in ("prefill", "ring"):
+        u = torch.rand(n, generator=g, device=device, dtype=torch.float32) - 0.5
+        v = -0.5 * torch.sign(u) * torch.log1p(-2.0 * u.abs()).clamp_min(-40.0)  # Laplace(0, 0.5)
+        if w.key == "prefill":
+            rows, hidden = w.shape
+            mult = torch.exp(torch.randn(rows, generator=g, device=device))
+            v = (v.view(rows, hidden) * mult[:, None]).reshape(-1)
+        else:
+            k = n // 2000
+            pos = torch.randperm(n, generator=g, device=device)[:k]
+            v[pos] *= 100.0
+    elif w.key == "smallblock":
+        v = torch.randn(n, generator=g, device=device) * 1e-3
+        v = (v.view(-1, 64) * torch.exp(2.0 * torch.randn(n // 64, generator=g, device=device))[:, None]).reshape(-1)
+    else:
+        raise KeyError(w.key)
+    return v.to(torch.bfloat16) if w.dtype == "bf16" else v

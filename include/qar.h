@@ -52,8 +52,8 @@
  *   - Any block-aligned sub-range of a valid call (pointers advanced by
  *     k*block elements and k scales) is itself a valid call with the same
  *     results in that range.
- *   - Thread-safe; the only global state is the per-thread text behind
- *     qar_last_error().
+ *   - Thread-safe; the only global state is per thread: the text behind
+ *     qar_last_error() and the pipelined call's cached HIP events.
  */
 #ifndef QAR_H
 #define QAR_H
@@ -124,7 +124,8 @@ qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* 
  * qar_reduce_quantized for every nchunks and nstreams.  Work on the side
  * streams starts after everything already enqueued on `stream`, and
  * `stream` waits for all chunks, so the caller sees one ordered operation on
- * `stream`.  The call creates and releases its HIP events.
+ * `stream`.  The call's HIP events are created on its first use per thread
+ * and device and reused afterwards (never device memory).
  *   nchunks   >= 1 (clipped to the number of blocks).
  *   streams   HOST array of nstreams hipStream_t (as void*), 1 .. QAR_MAX_STREAMS.
  */
