@@ -45,12 +45,62 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
 // ---------------------------------------------------------------------------
 // one-shot reduce: N quantized ranks -> requantized sum (+ optional dequant)
 
-template <int B>
+// Dequantized output of one wavefront's 1024-element tile, written so that
+// every 16-byte store instruction covers contiguous memory (1 KB per
+// instruction).  A lane holds 16 consecutive codes (32 bytes of bf16, 64 of
+// fp32), so the codes and scales of the wave are staged in LDS and each lane
+// reads back the 8 (bf16) or 4 (fp32) codes that belong to its store slots.
+// Only lanes of one wavefront exchange data, so a wave barrier suffices.
+template <int B, int OUT>
+__device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_t e0, size_t n, void* out,
+                                                       uint4* lds_codes, float* lds_scales) {
+    constexpr int kLanesPerBlock = B / kLaneElems;
+    const int lane = threadIdx.x & 63;
+    lds_codes[lane] = qo;
+    if (lane % kLanesPerBlock == 0) lds_scales[lane / kLanesPerBlock] = so;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const size_t wave0 = e0 - (size_t)lane * kLaneElems; // first element of the wave's tile
+    const int8_t* codes = reinterpret_cast<const int8_t*>(lds_codes);
+    if constexpr (OUT == kOutBF16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = 512 * j + 8 * lane; // element within the wave tile
+            const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
+            const float s = lds_scales[e / B];
+            uint4 o;
+            o.x = pack_bf16x2(code_f32(c.x, 0) * s, code_f32(c.x, 1) * s);
+            o.y = pack_bf16x2(code_f32(c.x, 2) * s, code_f32(c.x, 3) * s);
+            o.z = pack_bf16x2(code_f32(c.y, 0) * s, code_f32(c.y, 1) * s);
+            o.w = pack_bf16x2(code_f32(c.y, 2) * s, code_f32(c.y, 3) * s);
+            if (wave0 + e < n) store_b128(static_cast<uint16_t*>(out) + wave0 + e, o);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 256 * j + 4 * lane;
+            const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
+            const float s = lds_scales[e / B];
+            uint4 o;
+            o.x = __builtin_bit_cast(uint32_t, code_f32(c, 0) * s);
+            o.y = __builtin_bit_cast(uint32_t, code_f32(c, 1) * s);
+            o.z = __builtin_bit_cast(uint32_t, code_f32(c, 2) * s);
+            o.w = __builtin_bit_cast(uint32_t, code_f32(c, 3) * s);
+            if (wave0 + e < n) store_b128(static_cast<float*>(out) + wave0 + e, o);
+        }
+    }
+    // the next tile overwrites the staging area: keep this tile's reads first
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int B, int OUT>
 __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, size_t n,
                                                      int8_t* codes_out, float* scales_out,
-                                                     void* __restrict__ out, int out_kind,
-                                                     uint32_t ntiles) {
+                                                     void* __restrict__ out, uint32_t ntiles) {
     constexpr int G = 8; // ranks whose loads are in flight together
+    __shared__ uint4 lds_codes[OUT != kOutNone ? kThreads : 1];
+    __shared__ float lds_scales[OUT != kOutNone ? kThreads * kLaneElems / B : 1];
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
         const bool valid = e0 < n;
@@ -83,19 +133,15 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, si
             }
         }
         const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
-        uint32_t w[kLaneElems];
-        const uint4 qo = quantize16(acc, so, w);
+        const uint4 qo = quantize16(acc, so);
         if (valid) {
             store_b128(codes_out + e0, qo);
             if (e0 % B == 0) scales_out[blk] = so;
-            if (out_kind != kOutNone) {
-                float y[kLaneElems];
-                dequantize_words(w, so, y);
-                if (out_kind == kOutBF16)
-                    store16(static_cast<uint16_t*>(out) + e0, y);
-                else
-                    store16(static_cast<float*>(out) + e0, y);
-            }
+        }
+        if constexpr (OUT != kOutNone) {
+            const int wave = threadIdx.x / 64;
+            store_dequantized_tile<B, OUT>(qo, so, e0, n, out, lds_codes + wave * 64,
+                                           lds_scales + wave * (64 * kLaneElems / B));
         }
     }
 }
@@ -261,8 +307,15 @@ template <int B>
 hipError_t reduce_b(const RankPtrs& rp, int nranks, size_t n, int8_t* codes_out, float* scales_out,
                     void* out, int out_kind, hipStream_t st) {
     const Grid g = grid_for(n);
-    hipLaunchKernelGGL((k_reduce<B>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n, codes_out,
-                       scales_out, out, out_kind, g.ntiles);
+    if (out_kind == kOutBF16)
+        hipLaunchKernelGGL((k_reduce<B, kOutBF16>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
+                           codes_out, scales_out, out, g.ntiles);
+    else if (out_kind == kOutF32)
+        hipLaunchKernelGGL((k_reduce<B, kOutF32>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
+                           codes_out, scales_out, out, g.ntiles);
+    else
+        hipLaunchKernelGGL((k_reduce<B, kOutNone>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
+                           codes_out, scales_out, out, g.ntiles);
     return hipGetLastError();
 }
 
