@@ -281,4 +281,91 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_unquantized");
 }
 
+qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
+                                   uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
+                                   float* const* scales_work, void* out, uint32_t nchunks,
+                                   void* const* streams, uint32_t nstreams, void* stream) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_common(n, block);
+    if (st != QAR_OK) return st;
+    if (schedule != QAR_SCHEDULE_ONE_SHOT && schedule != QAR_SCHEDULE_RING) return QAR_ERR_UNSUPPORTED;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (!x || !codes_work || !scales_work || !out || !streams) return QAR_ERR_INVALID_ARG;
+    if (nranks == 0 || nranks > QAR_MAX_RANKS || nchunks == 0 || nstreams == 0 || nstreams > QAR_MAX_STREAMS)
+        return QAR_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nstreams; ++i)
+        if (!streams[i]) return QAR_ERR_INVALID_ARG;
+    const uint32_t nwork = schedule == QAR_SCHEDULE_ONE_SHOT ? nranks : 1;
+    const size_t nb = n / block, eb = dtype_bytes(dtype);
+    // every buffer the call touches; inputs may overlap each other, the
+    // workspaces and the output may overlap nothing
+    Range ins[QAR_MAX_RANKS], outs[2 * QAR_MAX_RANKS + 1];
+    int nouts = 0;
+    for (uint32_t r = 0; r < nranks; ++r) {
+        if (!x[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(x[r], 16)) return QAR_ERR_MISALIGNED;
+        ins[r] = range(x[r], n * eb);
+    }
+    for (uint32_t r = 0; r < nwork; ++r) {
+        if (!codes_work[r] || !scales_work[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(codes_work[r], 16) || !aligned(scales_work[r], 4)) return QAR_ERR_MISALIGNED;
+        outs[nouts++] = range(codes_work[r], n);
+        outs[nouts++] = range(scales_work[r], nb * 4);
+    }
+    if (!aligned(out, 16)) return QAR_ERR_MISALIGNED;
+    outs[nouts++] = range(out, n * eb);
+    for (int i = 0; i < nouts; ++i) {
+        for (int j = i + 1; j < nouts; ++j)
+            if (overlap(outs[i], outs[j])) return QAR_ERR_INVALID_ARG;
+        for (uint32_t r = 0; r < nranks; ++r)
+            if (overlap(outs[i], ins[r])) return QAR_ERR_INVALID_ARG;
+    }
+
+    const size_t chunks = nchunks < nb ? nchunks : nb;
+    const size_t per = (nb + chunks - 1) / chunks;
+    const uint32_t used = (uint32_t)(chunks < nstreams ? chunks : nstreams);
+    const int kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
+    const int okind = dtype == QAR_BF16 ? qar::kOutBF16 : qar::kOutF32;
+    const hipStream_t main_st = (hipStream_t)stream;
+
+    hipEvent_t* ev = nullptr;
+    hipError_t e = pipeline_events(&ev);
+    if (e != hipSuccess) return hip_fail(e, "qar_allreduce_simulated: events");
+    e = hipEventRecord(ev[0], main_st);
+    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) e = hipStreamWaitEvent((hipStream_t)streams[i], ev[0], 0);
+    for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
+        const size_t b0 = c * per;
+        if (b0 >= nb) break;
+        const size_t bn = (nb - b0 < per) ? nb - b0 : per, e0 = b0 * block, cn = bn * block;
+        const hipStream_t cs = (hipStream_t)streams[c % used];
+        const auto xin = [&](uint32_t r) { return (const void*)((const char*)x[r] + e0 * eb); };
+        void* const oc = (void*)((char*)out + e0 * eb);
+        if (schedule == QAR_SCHEDULE_ONE_SHOT) {
+            qar::RankPtrs rp;
+            memset(&rp, 0, sizeof rp);
+            for (uint32_t r = 0; e == hipSuccess && r < nranks; ++r) {
+                e = qar::launch_quantize(xin(r), kind, cn, (int)block, codes_work[r] + e0, scales_work[r] + b0, cs);
+                rp.codes[r] = codes_work[r] + e0;
+                rp.scales[r] = scales_work[r] + b0;
+            }
+            if (e == hipSuccess)
+                e = qar::launch_reduce(rp, (int)nranks, cn, (int)block, codes_work[0] + e0, scales_work[0] + b0, oc,
+                                       okind, cs);
+        } else {
+            const uint32_t s0 = (uint32_t)(c % nranks);
+            int8_t* const q = codes_work[0] + e0;
+            float* const sc = scales_work[0] + b0;
+            e = qar::launch_quantize(xin(s0), kind, cn, (int)block, q, sc, cs);
+            for (uint32_t k = 1; e == hipSuccess && k < nranks; ++k)
+                e = qar::launch_ring_step(q, sc, xin((s0 + k) % nranks), kind, cn, (int)block, q, sc, cs);
+            if (e == hipSuccess) e = qar::launch_dequantize(q, sc, cn, (int)block, oc, okind, cs);
+        }
+    }
+    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) {
+        e = hipEventRecord(ev[1 + i], (hipStream_t)streams[i]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, ev[1 + i], 0);
+    }
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_allreduce_simulated");
+}
+
 } // extern "C"

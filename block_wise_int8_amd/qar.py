@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qar.h")
 
 QAR_OK, QAR_ERR_INVALID_ARG, QAR_ERR_MISALIGNED, QAR_ERR_UNSUPPORTED, QAR_ERR_HIP = range(5)
 QAR_BF16, QAR_F32 = 0, 1
+QAR_SCHEDULE_ONE_SHOT, QAR_SCHEDULE_RING = 0, 1
 QAR_MAX_RANKS = 32
 QAR_MAX_STREAMS = 16
 BLOCK_SIZES = (64, 128, 256)
@@ -32,6 +33,7 @@ _SIGNATURES = {
     "qar_ring_step": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
     "qar_reduce_unquantized": [_vp, _u32, _sz, _int, _vp, _vp],
+    "qar_allreduce_simulated": [_vp, _int, _u32, _sz, _u32, _int, _vp, _vp, _vp, _u32, _vp, _u32, _vp],
     "qar_status_string": [_int],
     "qar_last_error": [],
 }
@@ -222,4 +224,36 @@ def qar_reduce_unquantized(xs: list[torch.Tensor], out: torch.Tensor | None = No
     ptrs = _ptrs(xs)
     _check(lib().qar_reduce_unquantized(ctypes.cast(ptrs, _vp), len(xs), n, _dtype_code(xs[0].dtype),
                                         _dev(out, "out").data_ptr(), _stream(stream)), "qar_reduce_unquantized")
+    return out
+
+
+def qar_allreduce_simulated(xs: list[torch.Tensor], block: int, schedule: str = "one_shot", nchunks: int = 1,
+                            streams: list | None = None, out: torch.Tensor | None = None,
+                            workspace: tuple | None = None, stream=None) -> torch.Tensor:
+    """The whole quantized AllReduce of N rank buffers on one GPU ('one_shot'
+    or 'ring'); returns the dequantized result every rank would hold.
+    ``workspace`` = (codes list, scales list) is allocated with torch when
+    not given."""
+    if not xs:
+        raise ValueError("need at least one rank")
+    for x in xs:
+        _dev(x, "x[r]")
+    sched = {"one_shot": QAR_SCHEDULE_ONE_SHOT, "ring": QAR_SCHEDULE_RING}[schedule]
+    n = xs[0].numel()
+    dev = xs[0].device
+    nwork = len(xs) if sched == QAR_SCHEDULE_ONE_SHOT else 1
+    if workspace is None:
+        workspace = ([torch.empty(n, dtype=torch.int8, device=dev) for _ in range(nwork)],
+                     [torch.empty(max(n // block, 1), dtype=torch.float32, device=dev) for _ in range(nwork)])
+    wc, ws = workspace
+    if out is None:
+        out = torch.empty(n, dtype=xs[0].dtype, device=dev)
+    if streams is None:
+        streams = [torch.cuda.current_stream()]
+    xp, cp, sp = _ptrs(xs), _ptrs(wc), _ptrs(ws)
+    sts = (ctypes.c_void_p * len(streams))(*[_stream(s) for s in streams])
+    _check(lib().qar_allreduce_simulated(ctypes.cast(xp, _vp), _dtype_code(xs[0].dtype), len(xs), n, block, sched,
+                                         ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), _dev(out, "out").data_ptr(),
+                                         nchunks, ctypes.cast(sts, _vp), len(streams), _stream(stream)),
+           "qar_allreduce_simulated")
     return out

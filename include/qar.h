@@ -173,6 +173,40 @@ qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, ui
 qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t n, qar_dtype dtype,
                                   void* out, void* stream);
 
+/*
+ * The whole quantized AllReduce of N rank buffers, simulated on one GPU:
+ * the result every rank of a real AllReduce would hold, computed with the
+ * calls above ("technical framework" steps 1-4, pipelined over chunks as in
+ * "key innovations" item 2).  The buffer is cut into `nchunks` block-aligned
+ * chunks; chunk c runs on streams[c % nstreams]:
+ *   QAR_SCHEDULE_ONE_SHOT: every rank's chunk is quantized
+ *     (codes_work[r], scales_work[r]), then one fused reduce in rank order
+ *     0..N-1 requantizes the sum in place into codes_work[0]/scales_work[0]
+ *     and writes its dequantized value to out.
+ *   QAR_SCHEDULE_RING: chunk c starts at rank s = c mod N, as the chunk
+ *     rank s injects first in a ring: quantize(x_s), then ring steps adding
+ *     x_{s+1}, ..., x_{s+N-1} (ranks mod N) in place in codes_work[0] /
+ *     scales_work[0], then dequantize to out.  With nchunks = N this is the
+ *     classic ring's reduce-scatter order; the all-gather forwards codes
+ *     unchanged, so it adds no error and is not simulated.
+ *   x            [in]  HOST array of nranks DEVICE pointers, n elements of dtype.
+ *   codes_work, scales_work  HOST arrays of DEVICE pointers: int8[n] and
+ *                float[n/block] workspaces; nranks of each for ONE_SHOT, only
+ *                [0] is used for RING (the rest may be NULL).
+ *   out          [out] n elements of dtype.
+ *   nchunks      >= 1 (clipped to the number of blocks); streams: HOST array
+ *                of 1..QAR_MAX_STREAMS handles; `stream` orders the whole call
+ *                as in qar_reduce_quantized_pipelined.
+ * Results are bit-identical for every nchunks and nstreams under ONE_SHOT;
+ * under RING they depend on nchunks through each chunk's starting rank.
+ */
+typedef enum qar_schedule { QAR_SCHEDULE_ONE_SHOT = 0, QAR_SCHEDULE_RING = 1 } qar_schedule;
+
+qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
+                                   uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
+                                   float* const* scales_work, void* out, uint32_t nchunks,
+                                   void* const* streams, uint32_t nstreams, void* stream);
+
 /* Static text for a status code. */
 const char* qar_status_string(qar_status status);
 

@@ -104,3 +104,23 @@ def test_unquantized_validation(L):
     assert u(_arr(A, B_ + 2), 2, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_MISALIGNED
     assert u(_arr(A, None), 2, 256, qar.QAR_BF16, C, None) == qar.QAR_ERR_INVALID_ARG
     assert u(xs, 2, 256, qar.QAR_BF16, A + 32, None) == qar.QAR_ERR_INVALID_ARG    # partial overlap
+
+
+def test_allreduce_simulated_validation(L):
+    f = L.qar_allreduce_simulated
+    xs, cw, sw, st = _arr(A, B_), _arr(C, D), _arr(0x50000, 0x60000), _arr(0x1234)
+    ok_args = (xs, qar.QAR_BF16, 2, 256, 256, qar.QAR_SCHEDULE_ONE_SHOT, cw, sw, 0x70000, 1, st, 1, None)
+    assert f(xs, qar.QAR_BF16, 2, 0, 256, 0, cw, sw, 0x70000, 1, st, 1, None) == qar.QAR_OK
+    bad = list(ok_args); bad[5] = 7
+    assert f(*bad) == qar.QAR_ERR_UNSUPPORTED                       # schedule
+    bad = list(ok_args); bad[9] = 0
+    assert f(*bad) == qar.QAR_ERR_INVALID_ARG                       # nchunks
+    bad = list(ok_args); bad[8] = B_ + 64
+    assert f(*bad) == qar.QAR_ERR_INVALID_ARG                       # out overlaps an input
+    bad = list(ok_args); bad[6] = _arr(C, C + 128)
+    assert f(*bad) == qar.QAR_ERR_INVALID_ARG                       # workspaces overlap
+    bad = list(ok_args); bad[6] = _arr(C, None)
+    assert f(*bad) == qar.QAR_ERR_INVALID_ARG                       # one-shot needs every rank's workspace
+    bad = list(ok_args); bad[5] = qar.QAR_SCHEDULE_RING; bad[6] = _arr(C, None); bad[7] = _arr(0x50000, None)
+    bad[8] = 0x70001
+    assert f(*bad) == qar.QAR_ERR_MISALIGNED                        # ring needs only [0]; out misaligned
