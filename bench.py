@@ -267,6 +267,7 @@ def main() -> int:
         result["ring_step"] = ring_bench(qar, torch, np, synth, dev)
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
+        result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, w, host, sets[0], torch)
@@ -448,6 +449,51 @@ def pipelined_bench(qar, torch, synth, dev, skew):
     best = min(sweep, key=lambda x: x["avg_us"])
     return {"workload": w.description + ", reduce without out", "sweep": sweep,
             "best": {k: best[k] for k in ("nchunks", "nstreams", "avg_us", "GBps", "hbm_frac")}}
+
+
+def allreduce_bench(qar, torch, synth, dev):
+    """The whole quantized AllReduce of the ring workload (N=4 x [2048, 3840]
+    bf16, block 256) simulated on one GPU, one-shot against ring (chunk c
+    starts at rank c mod N), over chunk/stream settings; error of the
+    dequantized result against the exact sum (fp64 on the GPU, for these
+    statistics only) next to the unquantized bf16 comparator's."""
+    w = synth.WORKLOADS["ring"]
+    N, n, B = w.nranks, w.n, w.block
+    xs = [synth.device_rank(w, r, dev) for r in range(N)]
+    exact = torch.zeros(n, dtype=torch.float64, device=dev)
+    for x in xs:
+        exact += x.double()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    wc = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(N)]
+    ws = [torch.empty(n // B, dtype=torch.float32, device=dev) for _ in range(N)]
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+
+    def err_stats(y):
+        d = (y.double() - exact).abs()
+        scale = exact.abs().mean().item()
+        return {"max_abs": round(d.max().item(), 5), "rms": round(d.square().mean().sqrt().item(), 6),
+                "rms_over_mean_abs_sum": round(d.square().mean().sqrt().item() / scale, 6)}
+
+    rows = []
+    for sched in ("one_shot", "ring"):
+        for nchunks, nstr in ((1, 1), (N, 1), (N, 4), (16, 4)):
+            if sched == "one_shot" and nchunks == N and nstr == 1:
+                continue
+
+            def fn(i, sched=sched, nchunks=nchunks, nstr=nstr):
+                qar.qar_allreduce_simulated(xs, B, sched, nchunks, streams[:nstr], out=out, workspace=(wc, ws))
+            us = _loop_us(torch, fn, 1, 20, warmup=30)
+            rows.append({"schedule": sched, "nchunks": nchunks, "nstreams": nstr, "avg_us": round(us, 2),
+                         "error": err_stats(out)})
+    def fb(i):
+        qar.qar_reduce_unquantized(xs, out=out)
+    us = _loop_us(torch, fb, 1, 50)
+    rows.append({"schedule": "unquantized bf16 reduce (comparator)", "avg_us": round(us, 2), "error": err_stats(out)})
+    del xs, wc, ws, exact
+    torch.cuda.empty_cache()
+    return {"workload": w.description + "; every rank's result computed on one GPU (no cache rotation: "
+                                        "the 127 MB of inputs stay in the 256 MB Infinity Cache)",
+            "runs": rows}
 
 
 def ring_bench(qar, torch, np, synth, dev):
