@@ -181,84 +181,115 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
 // ---------------------------------------------------------------------------
 // dequantize: codes, scales -> bf16 or fp32
 
+// Each 16-byte store instruction writes 1 KB of contiguous output: lane L of
+// a wavefront owns the store slots at elements 8L + 512j (bf16, j = 0..1) or
+// 4L + 256j (fp32, j = 0..3) of the wave's 1024-element tile and reads the
+// 8 or 4 codes of each slot directly (8 or 4 bytes, 512 or 256 bytes
+// contiguous per load instruction).
 template <int B, typename Out>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restrict__ codes,
                                                          const float* __restrict__ scales, size_t n,
                                                          Out* __restrict__ out, uint32_t ntiles) {
+    constexpr int kSlot = 16 / sizeof(Out);      // elements per 16-byte store
+    constexpr int kSlots = kLaneElems / kSlot;   // store slots per lane
+    const int lane = threadIdx.x & 63;
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
-        if (e0 >= n) continue;
-        const uint4 q = load_b128(codes + e0);
-        const float s = scales[e0 / B];
-        float y[kLaneElems];
-        dequantize16(q, s, y);
-        store16(out + e0, y);
+        const size_t wave0 = ((size_t)tile * kThreads + (threadIdx.x & ~63u)) * kLaneElems;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            const size_t e = wave0 + (size_t)j * 64 * kSlot + (size_t)lane * kSlot;
+            if (e >= n) continue; // n % 64 == 0: a slot is wholly inside or outside
+            const float s = scales[e / B];
+            uint4 o;
+            if constexpr (kSlot == 8) {
+                const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
+                o.x = pack_bf16x2(code_f32(c.x, 0) * s, code_f32(c.x, 1) * s);
+                o.y = pack_bf16x2(code_f32(c.x, 2) * s, code_f32(c.x, 3) * s);
+                o.z = pack_bf16x2(code_f32(c.y, 0) * s, code_f32(c.y, 1) * s);
+                o.w = pack_bf16x2(code_f32(c.y, 2) * s, code_f32(c.y, 3) * s);
+            } else {
+                const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
+                o.x = __builtin_bit_cast(uint32_t, code_f32(c, 0) * s);
+                o.y = __builtin_bit_cast(uint32_t, code_f32(c, 1) * s);
+                o.z = __builtin_bit_cast(uint32_t, code_f32(c, 2) * s);
+                o.w = __builtin_bit_cast(uint32_t, code_f32(c, 3) * s);
+            }
+            store_b128(out + e, o);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // the unquantized comparator: fp32 rank-order sum of N bf16/fp32 buffers
 
+// No block structure here, so every lane works on contiguous store slots:
+// lane L of a wavefront owns the 16-byte slots at elements
+// kSlot*L + 64*kSlot*j of the wave's 1024-element tile (kSlot = 8 for bf16,
+// 4 for fp32), and every load and store instruction covers 1 KB.
 template <typename T>
-struct RawVec; // one lane's 16 elements as 16-byte words
+struct SlotTraits;
 template <>
-struct RawVec<uint16_t> {
-    static constexpr int kWords = 2;
-    static constexpr int kGroup = 8; // ranks in flight together
+struct SlotTraits<uint16_t> {
+    static constexpr int kSlot = 8;
+    static constexpr int kGroup = 8; // ranks whose loads are in flight together
+    static __device__ __forceinline__ void widen(uint4 w, float* v) {
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf16_lo(a[k]);
+            v[2 * k + 1] = bf16_hi(a[k]);
+        }
+    }
+    static __device__ __forceinline__ uint4 narrow(const float* v) {
+        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7]));
+    }
 };
 template <>
-struct RawVec<float> {
-    static constexpr int kWords = 4;
+struct SlotTraits<float> {
+    static constexpr int kSlot = 4;
     static constexpr int kGroup = 4;
+    static __device__ __forceinline__ void widen(uint4 w, float* v) {
+        v[0] = __builtin_bit_cast(float, w.x);
+        v[1] = __builtin_bit_cast(float, w.y);
+        v[2] = __builtin_bit_cast(float, w.z);
+        v[3] = __builtin_bit_cast(float, w.w);
+    }
+    static __device__ __forceinline__ uint4 narrow(const float* v) {
+        return make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                          __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3]));
+    }
 };
-
-template <typename T>
-__device__ __forceinline__ void widen(const uint4 (&raw)[RawVec<T>::kWords], float (&v)[kLaneElems]);
-
-template <>
-__device__ __forceinline__ void widen<uint16_t>(const uint4 (&raw)[2], float (&v)[kLaneElems]) {
-    const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        v[2 * j] = bf16_lo(w[j]);
-        v[2 * j + 1] = bf16_hi(w[j]);
-    }
-}
-
-template <>
-__device__ __forceinline__ void widen<float>(const uint4 (&raw)[4], float (&v)[kLaneElems]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[4 * j + 0] = __builtin_bit_cast(float, raw[j].x);
-        v[4 * j + 1] = __builtin_bit_cast(float, raw[j].y);
-        v[4 * j + 2] = __builtin_bit_cast(float, raw[j].z);
-        v[4 * j + 3] = __builtin_bit_cast(float, raw[j].w);
-    }
-}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_reduce_unquantized(PlainPtrs xp, int nranks, size_t n, T* out,
                                                                  uint32_t ntiles) {
-    constexpr int W = RawVec<T>::kWords, G = RawVec<T>::kGroup;
+    using S = SlotTraits<T>;
+    constexpr int kSlot = S::kSlot, kSlots = kLaneElems / kSlot, G = S::kGroup;
+    const int lane = threadIdx.x & 63;
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
-        const bool valid = e0 < n;
-        const size_t ld = valid ? e0 : 0; // see k_quantize
+        const size_t wave0 = ((size_t)tile * kThreads + (threadIdx.x & ~63u)) * kLaneElems;
+        size_t e[kSlots], ld[kSlots];
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j) {
+            e[j] = wave0 + (size_t)j * 64 * kSlot + (size_t)lane * kSlot;
+            ld[j] = e[j] < n ? e[j] : 0; // n % 16 == 0: a slot is wholly inside or outside
+        }
         float acc[kLaneElems];
         for (int g = 0; g < nranks; g += G) {
-            uint4 raw[G][W];
+            uint4 raw[G][kSlots];
 #pragma unroll
-            for (int j = 0; j < G; ++j)
-                if (g + j < nranks)
+            for (int r = 0; r < G; ++r)
+                if (g + r < nranks)
 #pragma unroll
-                    for (int k = 0; k < W; ++k)
-                        raw[j][k] = load_b128(static_cast<const T*>(xp.x[g + j]) + ld + k * (kLaneElems / W));
+                    for (int j = 0; j < kSlots; ++j) raw[r][j] = load_b128(static_cast<const T*>(xp.x[g + r]) + ld[j]);
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                if (g + j < nranks) {
+            for (int r = 0; r < G; ++r) {
+                if (g + r < nranks) {
                     float v[kLaneElems];
-                    widen<T>(raw[j], v);
-                    if (g + j == 0) {
+#pragma unroll
+                    for (int j = 0; j < kSlots; ++j) S::widen(raw[r][j], v + j * kSlot);
+                    if (g + r == 0) {
 #pragma unroll
                         for (int i = 0; i < kLaneElems; ++i) acc[i] = v[i];
                     } else {
@@ -268,7 +299,9 @@ __global__ __launch_bounds__(kThreads) void k_reduce_unquantized(PlainPtrs xp, i
                 }
             }
         }
-        if (valid) store16(out + e0, acc);
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j)
+            if (e[j] < n) store_b128(out + e[j], S::narrow(acc + j * kSlot));
     }
 }
 
