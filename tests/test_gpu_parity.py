@@ -317,6 +317,27 @@ def test_allreduce_simulated(oracle_lib, schedule, nranks, nchunks, nstreams, dt
 # contract details
 
 
+def test_concurrent_streams_and_repeat_runs(oracle_lib):
+    """Two reduces on two streams at once, each repeated: every run equals
+    the oracle (no shared state between calls, deterministic results)."""
+    block, n = 256, ragged_n(256, tiles=8)
+    jobs = []
+    for k in range(2):
+        xs = [mixed_bf16(1000 + 10 * k + r, n, block, SUM_OUTLIER) for r in range(4)]
+        codes, scales = _rank_codes(oracle_lib, xs, block)
+        jobs.append(([to_dev(c) for c in codes], [to_dev(s) for s in scales], oracle_lib.reduce(codes, scales, block)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for (dc, ds, _), st_ in zip(jobs, streams):
+            outs.append(qar.qar_reduce_quantized(dc, ds, block, stream=st_))
+    torch.cuda.synchronize()
+    for i, (c, s) in enumerate(outs):
+        wc, ws = jobs[i % 2][2]
+        assert_same_codes(to_host(c), wc, f"run {i} codes")
+        assert_same_f32(to_host(s), ws, f"run {i} scales")
+
+
 def test_subrange_call_equals_slice(oracle_lib):
     """A block-aligned sub-range (offset pointers) is a valid call with the
     same results in that range."""
