@@ -328,6 +328,7 @@ def test_concurrent_streams_and_repeat_runs(oracle_lib):
         jobs.append(([to_dev(c) for c in codes], [to_dev(s) for s in scales], oracle_lib.reduce(codes, scales, block)))
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     outs = []
+    torch.cuda.synchronize()            # inputs were copied on the default stream
     for rep in range(3):
         for (dc, ds, _), st_ in zip(jobs, streams):
             outs.append(qar.qar_reduce_quantized(dc, ds, block, stream=st_))
