@@ -369,3 +369,163 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
 }
 
 } // extern "C"
+
+// ---------------------------------------------------------------------------
+// row-bounded blocks
+
+namespace {
+
+struct RowShape {
+    size_t rows, row_len, per_row, nblocks, n;
+};
+
+qar_status row_shape(size_t rows, size_t row_len, uint32_t block, RowShape& sh) {
+    if (!block_supported(block)) return QAR_ERR_UNSUPPORTED;
+    if (row_len != 0 && rows > QAR_MAX_ELEMENTS / row_len) return QAR_ERR_INVALID_ARG;
+    sh.rows = rows;
+    sh.row_len = row_len;
+    sh.per_row = (row_len + block - 1) / block;
+    sh.n = rows * row_len;
+    sh.nblocks = rows * sh.per_row;
+    if (sh.nblocks > QAR_MAX_ROW_BLOCKS) return QAR_ERR_INVALID_ARG;
+    return QAR_OK;
+}
+
+bool flat_ok(const RowShape& sh, uint32_t block) { return sh.row_len % block == 0; }
+
+qar::RowsCall rows_call(int op, const RowShape& sh, uint32_t block) {
+    qar::RowsCall c;
+    memset(&c, 0, sizeof c);
+    c.op = op;
+    c.rows = sh.rows;
+    c.row_len = sh.row_len;
+    c.block = (int)block;
+    return c;
+}
+
+} // namespace
+
+extern "C" {
+
+qar_status qar_quantize_rows(const void* x, qar_dtype dtype, size_t rows, size_t row_len, uint32_t block,
+                             int8_t* codes, float* scales, void* stream) {
+    RowShape sh;
+    qar_status st = row_shape(rows, row_len, block, sh);
+    if (st != QAR_OK || sh.n == 0) return st;
+    if (!x || !codes || !scales) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (flat_ok(sh, block) && aligned(x, 16) && aligned(codes, 16))
+        return qar_quantize_blocks(x, dtype, sh.n, block, codes, scales, stream);
+    if (!aligned(x, dtype_bytes(dtype)) || !aligned(scales, 4)) return QAR_ERR_MISALIGNED;
+    const Range xi = range(x, sh.n * dtype_bytes(dtype)), co = range(codes, sh.n), so = range(scales, sh.nblocks * 4);
+    if (overlap(xi, co) || overlap(xi, so) || overlap(co, so)) return QAR_ERR_INVALID_ARG;
+    qar::RowsCall c = rows_call(qar::kRowsQuantize, sh, block);
+    c.kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
+    c.x = x;
+    c.codes_out = codes;
+    c.scales_out = scales;
+    const hipError_t e = qar::launch_rows(c, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_quantize_rows");
+}
+
+qar_status qar_dequantize_rows(const int8_t* codes, const float* scales, size_t rows, size_t row_len,
+                               uint32_t block, void* out, qar_dtype out_dtype, void* stream) {
+    RowShape sh;
+    qar_status st = row_shape(rows, row_len, block, sh);
+    if (st != QAR_OK || sh.n == 0) return st;
+    if (!codes || !scales || !out) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(out_dtype)) return QAR_ERR_UNSUPPORTED;
+    if (flat_ok(sh, block) && aligned(codes, 16) && aligned(out, 16))
+        return qar_dequantize(codes, scales, sh.n, block, out, out_dtype, stream);
+    if (!aligned(out, dtype_bytes(out_dtype)) || !aligned(scales, 4)) return QAR_ERR_MISALIGNED;
+    const Range ci = range(codes, sh.n), si = range(scales, sh.nblocks * 4),
+                oo = range(out, sh.n * dtype_bytes(out_dtype));
+    if (overlap(oo, ci) || overlap(oo, si)) return QAR_ERR_INVALID_ARG;
+    qar::RowsCall c = rows_call(qar::kRowsDequantize, sh, block);
+    c.kind = out_dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
+    c.codes_in = codes;
+    c.scales_in = scales;
+    c.out = out;
+    const hipError_t e = qar::launch_rows(c, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_dequantize_rows");
+}
+
+qar_status qar_reduce_quantized_rows(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t rows, size_t row_len, uint32_t block, int8_t* codes_out,
+                                     float* scales_out, void* out, qar_dtype out_dtype, void* stream) {
+    RowShape sh;
+    qar_status st = row_shape(rows, row_len, block, sh);
+    if (st != QAR_OK || sh.n == 0) return st;
+    if (!codes || !scales || !codes_out || !scales_out) return QAR_ERR_INVALID_ARG;
+    if (nranks == 0 || nranks > QAR_MAX_RANKS) return QAR_ERR_INVALID_ARG;
+    if (out && !dtype_ok(out_dtype)) return QAR_ERR_UNSUPPORTED;
+    if (flat_ok(sh, block)) {
+        bool al = aligned(codes_out, 16) && (!out || aligned(out, 16));
+        for (uint32_t r = 0; al && r < nranks; ++r) al = codes[r] && aligned(codes[r], 16);
+        if (al)
+            return qar_reduce_quantized(codes, scales, nranks, sh.n, block, codes_out, scales_out, out, out_dtype,
+                                        stream);
+    }
+    if (!aligned(scales_out, 4) || (out && !aligned(out, dtype_bytes(out_dtype)))) return QAR_ERR_MISALIGNED;
+    const Range co = range(codes_out, sh.n), so = range(scales_out, sh.nblocks * 4);
+    if (overlap(co, so)) return QAR_ERR_INVALID_ARG;
+    Range oo{0, 0};
+    if (out) {
+        oo = range(out, sh.n * dtype_bytes(out_dtype));
+        if (overlap(oo, co) || overlap(oo, so)) return QAR_ERR_INVALID_ARG;
+    }
+    qar::RowsCall c = rows_call(qar::kRowsReduce, sh, block);
+    int same_codes = -1, same_scales = -1;
+    for (uint32_t r = 0; r < nranks; ++r) {
+        if (!codes[r] || !scales[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(scales[r], 4)) return QAR_ERR_MISALIGNED;
+        const Range ci = range(codes[r], sh.n), si = range(scales[r], sh.nblocks * 4);
+        if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci))
+            return QAR_ERR_INVALID_ARG;
+        if (out && (overlap(oo, ci) || overlap(oo, si))) return QAR_ERR_INVALID_ARG;
+        if (co.lo == ci.lo) same_codes = (int)r;
+        if (so.lo == si.lo) same_scales = (int)r;
+        c.rp.codes[r] = codes[r];
+        c.rp.scales[r] = scales[r];
+    }
+    if (same_codes != same_scales) return QAR_ERR_INVALID_ARG;
+    c.kind = (out && out_dtype == QAR_F32) ? qar::kInF32 : qar::kInBF16;
+    c.nranks = (int)nranks;
+    c.codes_out = codes_out;
+    c.scales_out = scales_out;
+    c.out = out;
+    const hipError_t e = qar::launch_rows(c, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_rows");
+}
+
+qar_status qar_ring_step_rows(const int8_t* codes_in, const float* scales_in, const void* local, qar_dtype dtype,
+                              size_t rows, size_t row_len, uint32_t block, int8_t* codes_out, float* scales_out,
+                              void* stream) {
+    RowShape sh;
+    qar_status st = row_shape(rows, row_len, block, sh);
+    if (st != QAR_OK || sh.n == 0) return st;
+    if (!codes_in || !scales_in || !local || !codes_out || !scales_out) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (flat_ok(sh, block) && aligned(codes_in, 16) && aligned(codes_out, 16) && aligned(local, 16))
+        return qar_ring_step(codes_in, scales_in, local, dtype, sh.n, block, codes_out, scales_out, stream);
+    if (!aligned(local, dtype_bytes(dtype)) || !aligned(scales_in, 4) || !aligned(scales_out, 4))
+        return QAR_ERR_MISALIGNED;
+    const Range ci = range(codes_in, sh.n), si = range(scales_in, sh.nblocks * 4),
+                li = range(local, sh.n * dtype_bytes(dtype)), co = range(codes_out, sh.n),
+                so = range(scales_out, sh.nblocks * 4);
+    if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci) ||
+        overlap(co, li) || overlap(so, li) || overlap(co, so))
+        return QAR_ERR_INVALID_ARG;
+    if ((co.lo == ci.lo) != (so.lo == si.lo)) return QAR_ERR_INVALID_ARG;
+    qar::RowsCall c = rows_call(qar::kRowsRingStep, sh, block);
+    c.kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
+    c.x = local;
+    c.codes_in = codes_in;
+    c.scales_in = scales_in;
+    c.codes_out = codes_out;
+    c.scales_out = scales_out;
+    const hipError_t e = qar::launch_rows(c, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_ring_step_rows");
+}
+
+} // extern "C"

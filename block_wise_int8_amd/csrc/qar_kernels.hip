@@ -306,6 +306,184 @@ __global__ __launch_bounds__(kThreads) void k_reduce_unquantized(PlainPtrs xp, i
 }
 
 // ---------------------------------------------------------------------------
+// row-bounded blocks: a [rows, row_len] tensor whose rows restart the block
+// grid, so the last block of a row may be partial (row_len % B elements).
+// One wavefront per block; lane l owns the block's elements l, l+64, l+128,
+// l+192 (B <= 256).  Elements move one by one (each access instruction is
+// still contiguous across the wave); this is the general path, taken only
+// when row_len % B != 0.
+
+struct RowMap {
+    size_t rows, row_len;
+    uint32_t block, per_row; // per_row = ceil(row_len / block)
+    __device__ __forceinline__ void locate(size_t b, size_t& start, uint32_t& len) const {
+        const size_t r = b / per_row, k = b % per_row;
+        const size_t col = k * block;
+        start = r * row_len + col;
+        len = (uint32_t)(row_len - col < block ? row_len - col : block);
+    }
+};
+
+__device__ __forceinline__ float wave_max(float m) {
+    m = fmaxf(m, dpp_move<kDppSwapAdjacent>(m));
+    m = fmaxf(m, dpp_move<kDppSwapPairs>(m));
+    m = fmaxf(m, dpp_move<kDppRowHalfMirror>(m));
+    m = fmaxf(m, dpp_move<kDppRowMirror>(m));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    return m;
+}
+
+__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) {
+    return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
+}
+__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) {
+    p[i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+}
+__device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
+
+constexpr int kRowSlots = 4; // elements per lane (B <= 256)
+
+// codes of v[0..3] for scale s (same arithmetic as quantize16)
+__device__ __forceinline__ void quantize4(const float (&v)[kRowSlots], float s, int8_t (&q)[kRowSlots]) {
+    if (s >= kFastQuotientMinScale) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int t = 0; t < kRowSlots; ++t) {
+            float y = v[t] * r;
+            const float e = __builtin_fmaf(-y, s, v[t]);
+            y = __builtin_fmaf(e, r, y);
+            q[t] = (int8_t)(code_bits_of(y) & 0xFFu);
+        }
+    } else if (s != 0.0f) {
+#pragma unroll
+        for (int t = 0; t < kRowSlots; ++t) q[t] = (int8_t)(code_bits_of(v[t] / s) & 0xFFu);
+    } else {
+#pragma unroll
+        for (int t = 0; t < kRowSlots; ++t) q[t] = 0;
+    }
+}
+
+__device__ __forceinline__ size_t wave_block_index() {
+    return (size_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void k_quantize_rows(const In* __restrict__ x, RowMap map, size_t nblocks,
+                                                            int8_t* __restrict__ codes, float* __restrict__ scales) {
+    const size_t b = wave_block_index();
+    if (b >= nblocks) return; // whole wavefronts leave together
+    const int lane = threadIdx.x & 63;
+    size_t start;
+    uint32_t len;
+    map.locate(b, start, len);
+    float v[kRowSlots];
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        v[t] = i < len ? load_elem(x, start + i) : 0.0f;
+        m = fmaxf(m, fabsf(v[t]));
+    }
+    const float s = wave_max(m) / 127.0f;
+    int8_t q[kRowSlots];
+    quantize4(v, s, q);
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        if (i < len) codes[start + i] = q[t];
+    }
+    if (lane == 0) scales[b] = s;
+}
+
+template <typename Out>
+__global__ __launch_bounds__(kThreads) void k_dequantize_rows(const int8_t* __restrict__ codes,
+                                                              const float* __restrict__ scales, RowMap map,
+                                                              size_t nblocks, Out* __restrict__ out) {
+    const size_t b = wave_block_index();
+    if (b >= nblocks) return;
+    const int lane = threadIdx.x & 63;
+    size_t start;
+    uint32_t len;
+    map.locate(b, start, len);
+    const float s = scales[b];
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        if (i < len) store_elem(out, start + i, (float)codes[start + i] * s);
+    }
+}
+
+template <typename Out>
+__global__ __launch_bounds__(kThreads) void k_reduce_rows(RankPtrs rp, int nranks, RowMap map, size_t nblocks,
+                                                          int8_t* codes_out, float* scales_out, Out* out) {
+    const size_t b = wave_block_index();
+    if (b >= nblocks) return;
+    const int lane = threadIdx.x & 63;
+    size_t start;
+    uint32_t len;
+    map.locate(b, start, len);
+    float acc[kRowSlots];
+    for (int r = 0; r < nranks; ++r) {
+        const float s = rp.scales[r][b];
+#pragma unroll
+        for (int t = 0; t < kRowSlots; ++t) {
+            const uint32_t i = lane + 64 * t;
+            const float y = i < len ? (float)rp.codes[r][start + i] * s : 0.0f;
+            acc[t] = r == 0 ? y : acc[t] + y;
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) m = fmaxf(m, fabsf(acc[t]));
+    const float so = wave_max(m) / 127.0f;
+    int8_t q[kRowSlots];
+    quantize4(acc, so, q);
+    // every lane has read its inputs (the reduction above waited for them),
+    // so writing in place over rank buffers is safe
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        if (i < len) {
+            codes_out[start + i] = q[t];
+            if (out) store_elem(out, start + i, (float)q[t] * so);
+        }
+    }
+    if (lane == 0) scales_out[b] = so;
+}
+
+template <typename In>
+__global__ __launch_bounds__(kThreads) void k_ring_step_rows(const int8_t* codes_in, const float* scales_in,
+                                                             const In* __restrict__ local, RowMap map, size_t nblocks,
+                                                             int8_t* codes_out, float* scales_out) {
+    const size_t b = wave_block_index();
+    if (b >= nblocks) return;
+    const int lane = threadIdx.x & 63;
+    size_t start;
+    uint32_t len;
+    map.locate(b, start, len);
+    const float s = scales_in[b];
+    float acc[kRowSlots];
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        acc[t] = i < len ? (float)codes_in[start + i] * s + load_elem(local, start + i) : 0.0f;
+        m = fmaxf(m, fabsf(acc[t]));
+    }
+    const float so = wave_max(m) / 127.0f;
+    int8_t q[kRowSlots];
+    quantize4(acc, so, q);
+#pragma unroll
+    for (int t = 0; t < kRowSlots; ++t) {
+        const uint32_t i = lane + 64 * t;
+        if (i < len) codes_out[start + i] = q[t];
+    }
+    if (lane == 0) scales_out[b] = so;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 namespace {
@@ -380,7 +558,54 @@ hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void
     return hipGetLastError();
 }
 
+uint32_t row_grid(size_t nblocks) { return (uint32_t)((nblocks + kThreads / 64 - 1) / (kThreads / 64)); }
+
 } // namespace
+
+hipError_t launch_rows(const RowsCall& c, hipStream_t st) {
+    RowMap map;
+    map.rows = c.rows;
+    map.row_len = c.row_len;
+    map.block = (uint32_t)c.block;
+    map.per_row = (uint32_t)((c.row_len + c.block - 1) / c.block);
+    const size_t nblocks = c.rows * map.per_row;
+    const dim3 grid(row_grid(nblocks)), threads(kThreads);
+    switch (c.op) {
+    case kRowsQuantize:
+        if (c.kind == kInBF16)
+            hipLaunchKernelGGL((k_quantize_rows<uint16_t>), grid, threads, 0, st, static_cast<const uint16_t*>(c.x),
+                               map, nblocks, c.codes_out, c.scales_out);
+        else
+            hipLaunchKernelGGL((k_quantize_rows<float>), grid, threads, 0, st, static_cast<const float*>(c.x), map,
+                               nblocks, c.codes_out, c.scales_out);
+        break;
+    case kRowsDequantize:
+        if (c.kind == kInBF16)
+            hipLaunchKernelGGL((k_dequantize_rows<uint16_t>), grid, threads, 0, st, c.codes_in, c.scales_in, map,
+                               nblocks, static_cast<uint16_t*>(c.out));
+        else
+            hipLaunchKernelGGL((k_dequantize_rows<float>), grid, threads, 0, st, c.codes_in, c.scales_in, map,
+                               nblocks, static_cast<float*>(c.out));
+        break;
+    case kRowsReduce:
+        if (c.kind == kInBF16)
+            hipLaunchKernelGGL((k_reduce_rows<uint16_t>), grid, threads, 0, st, c.rp, c.nranks, map, nblocks,
+                               c.codes_out, c.scales_out, static_cast<uint16_t*>(c.out));
+        else
+            hipLaunchKernelGGL((k_reduce_rows<float>), grid, threads, 0, st, c.rp, c.nranks, map, nblocks,
+                               c.codes_out, c.scales_out, static_cast<float*>(c.out));
+        break;
+    default:
+        if (c.kind == kInBF16)
+            hipLaunchKernelGGL((k_ring_step_rows<uint16_t>), grid, threads, 0, st, c.codes_in, c.scales_in,
+                               static_cast<const uint16_t*>(c.x), map, nblocks, c.codes_out, c.scales_out);
+        else
+            hipLaunchKernelGGL((k_ring_step_rows<float>), grid, threads, 0, st, c.codes_in, c.scales_in,
+                               static_cast<const float*>(c.x), map, nblocks, c.codes_out, c.scales_out);
+        break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
                                      hipStream_t st) {

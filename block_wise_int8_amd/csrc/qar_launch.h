@@ -24,6 +24,24 @@ struct PlainPtrs {
     const void* x[kMaxRanks];
 };
 
+// The row-bounded general path (one wavefront per block).
+enum : int { kRowsQuantize = 0, kRowsDequantize = 1, kRowsReduce = 2, kRowsRingStep = 3 };
+struct RowsCall {
+    int op;
+    int kind;                 // element type of x / out (kInBF16 or kInF32)
+    size_t rows, row_len;
+    int block;
+    const void* x;            // quantize: input; ring step: local
+    const int8_t* codes_in;   // dequantize, ring step
+    const float* scales_in;
+    RankPtrs rp;              // reduce
+    int nranks;
+    int8_t* codes_out;
+    float* scales_out;
+    void* out;                // dequantize; reduce (optional, may be null)
+};
+hipError_t launch_rows(const RowsCall& c, hipStream_t st);
+
 hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
                                      hipStream_t st);
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,

@@ -33,6 +33,10 @@ _SIGNATURES = {
     "qar_ring_step": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
     "qar_reduce_unquantized": [_vp, _u32, _sz, _int, _vp, _vp],
+    "qar_quantize_rows": [_vp, _int, _sz, _sz, _u32, _vp, _vp, _vp],
+    "qar_reduce_quantized_rows": [_vp, _vp, _u32, _sz, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_ring_step_rows": [_vp, _vp, _vp, _int, _sz, _sz, _u32, _vp, _vp, _vp],
+    "qar_dequantize_rows": [_vp, _vp, _sz, _sz, _u32, _vp, _int, _vp],
     "qar_allreduce_simulated": [_vp, _int, _u32, _sz, _u32, _int, _vp, _vp, _vp, _u32, _vp, _u32, _vp],
     "qar_status_string": [_int],
     "qar_last_error": [],
@@ -256,4 +260,77 @@ def qar_allreduce_simulated(xs: list[torch.Tensor], block: int, schedule: str = 
                                          ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), _dev(out, "out").data_ptr(),
                                          nchunks, ctypes.cast(sts, _vp), len(streams), _stream(stream)),
            "qar_allreduce_simulated")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# row-bounded blocks ([rows, row_len] tensors; the block grid restarts per row)
+
+
+def row_blocks(rows: int, row_len: int, block: int) -> int:
+    return rows * (-(-row_len // block))
+
+
+def qar_quantize_rows(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None, stream=None):
+    """x: [rows, row_len] bf16/fp32 -> (codes [rows*row_len], scales [rows*ceil(row_len/block)])."""
+    _dev(x, "x")
+    rows, row_len = x.shape
+    if codes is None:
+        codes = torch.empty(rows * row_len, dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty(max(row_blocks(rows, row_len, block), 1), dtype=torch.float32, device=x.device)
+    _check(lib().qar_quantize_rows(x.data_ptr(), _dtype_code(x.dtype), rows, row_len, block,
+                                   _dev(codes, "codes").data_ptr(), _dev(scales, "scales").data_ptr(),
+                                   _stream(stream)), "qar_quantize_rows")
+    return codes, scales
+
+
+def qar_reduce_quantized_rows(codes: list[torch.Tensor], scales: list[torch.Tensor], rows: int, row_len: int,
+                              block: int, codes_out: torch.Tensor | None = None,
+                              scales_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None):
+    if len(codes) != len(scales) or not codes:
+        raise ValueError("need one scales tensor per codes tensor, at least one rank")
+    for c, s in zip(codes, scales):
+        _dev(c, "codes[r]")
+        _dev(s, "scales[r]")
+    dev = codes[0].device
+    if codes_out is None:
+        codes_out = torch.empty(rows * row_len, dtype=torch.int8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(row_blocks(rows, row_len, block), 1), dtype=torch.float32, device=dev)
+    optr, odt = _out_args(out)
+    cp, sp = _ptrs(codes), _ptrs(scales)
+    _check(lib().qar_reduce_quantized_rows(ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), len(codes), rows, row_len,
+                                           block, _dev(codes_out, "codes_out").data_ptr(),
+                                           _dev(scales_out, "scales_out").data_ptr(), optr, odt, _stream(stream)),
+           "qar_reduce_quantized_rows")
+    return codes_out, scales_out
+
+
+def qar_ring_step_rows(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
+                       codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
+    """local: [rows, row_len]; codes/scales in the row-bounded layout."""
+    _dev(codes_in, "codes_in"), _dev(scales_in, "scales_in"), _dev(local, "local")
+    rows, row_len = local.shape
+    if codes_out is None:
+        codes_out = torch.empty(rows * row_len, dtype=torch.int8, device=local.device)
+    if scales_out is None:
+        scales_out = torch.empty(max(row_blocks(rows, row_len, block), 1), dtype=torch.float32, device=local.device)
+    _check(lib().qar_ring_step_rows(codes_in.data_ptr(), scales_in.data_ptr(), local.data_ptr(),
+                                    _dtype_code(local.dtype), rows, row_len, block,
+                                    _dev(codes_out, "codes_out").data_ptr(), _dev(scales_out, "scales_out").data_ptr(),
+                                    _stream(stream)), "qar_ring_step_rows")
+    return codes_out, scales_out
+
+
+def qar_dequantize_rows(codes: torch.Tensor, scales: torch.Tensor, rows: int, row_len: int, block: int,
+                        out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                        stream=None) -> torch.Tensor:
+    _dev(codes, "codes"), _dev(scales, "scales")
+    if out is None:
+        out = torch.empty(rows, row_len, dtype=out_dtype, device=codes.device)
+    _check(lib().qar_dequantize_rows(codes.data_ptr(), scales.data_ptr(), rows, row_len, block,
+                                     _dev(out, "out").data_ptr(), _dtype_code(out.dtype), _stream(stream)),
+           "qar_dequantize_rows")
     return out

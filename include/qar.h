@@ -207,6 +207,34 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
                                    float* const* scales_work, void* out, uint32_t nchunks,
                                    void* const* streams, uint32_t nstreams, void* stream);
 
+/*
+ * Row-bounded blocks: the same four operations on a [rows, row_len] tensor
+ * whose block grid restarts at every row, so the last block of a row holds
+ * row_len % block elements when row_len is not a multiple of block (a block
+ * never spans two rows).  Each row has per_row = ceil(row_len / block)
+ * blocks; scales hold rows * per_row values, row-major; codes and data hold
+ * rows * row_len elements, row-major.  The arithmetic of every block is that
+ * of the calls above, a partial block taking its absmax over its own
+ * elements.  When row_len % block == 0 the block grids coincide and the call
+ * is exactly the flat call with n = rows * row_len.
+ * Requirements: block 64, 128 or 256; rows * row_len <= QAR_MAX_ELEMENTS;
+ * rows * per_row <= QAR_MAX_ROW_BLOCKS; data pointers aligned to their
+ * element size, scales to 4 bytes, codes unconstrained (the flat fast path
+ * is taken when the flat call's 16-byte alignment also holds).
+ */
+#define QAR_MAX_ROW_BLOCKS ((size_t)1 << 26)
+
+qar_status qar_quantize_rows(const void* x, qar_dtype dtype, size_t rows, size_t row_len, uint32_t block,
+                             int8_t* codes, float* scales, void* stream);
+qar_status qar_reduce_quantized_rows(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t rows, size_t row_len, uint32_t block, int8_t* codes_out,
+                                     float* scales_out, void* out, qar_dtype out_dtype, void* stream);
+qar_status qar_ring_step_rows(const int8_t* codes_in, const float* scales_in, const void* local, qar_dtype dtype,
+                              size_t rows, size_t row_len, uint32_t block, int8_t* codes_out, float* scales_out,
+                              void* stream);
+qar_status qar_dequantize_rows(const int8_t* codes, const float* scales, size_t rows, size_t row_len,
+                               uint32_t block, void* out, qar_dtype out_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* qar_status_string(qar_status status);
 

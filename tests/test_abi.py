@@ -124,3 +124,21 @@ def test_allreduce_simulated_validation(L):
     bad = list(ok_args); bad[5] = qar.QAR_SCHEDULE_RING; bad[6] = _arr(C, None); bad[7] = _arr(0x50000, None)
     bad[8] = 0x70001
     assert f(*bad) == qar.QAR_ERR_MISALIGNED                        # ring needs only [0]; out misaligned
+
+
+def test_rows_validation(L):
+    q = L.qar_quantize_rows
+    assert q(A, qar.QAR_BF16, 0, 100, 256, B_, C, None) == qar.QAR_OK
+    assert q(A, qar.QAR_BF16, 3, 100, 100, B_, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert q(A + 1, qar.QAR_BF16, 3, 100, 256, B_, C, None) == qar.QAR_ERR_MISALIGNED   # bf16 needs 2-byte alignment
+    assert q(A, qar.QAR_F32, 3, 100, 256, B_, C + 2, None) == qar.QAR_ERR_MISALIGNED
+    assert q(A, qar.QAR_BF16, 3, 100, 256, A + 64, C, None) == qar.QAR_ERR_INVALID_ARG   # codes overlap x
+    assert q(A, qar.QAR_BF16, 1 << 20, 1 << 21, 64, B_, C, None) == qar.QAR_ERR_INVALID_ARG   # too many elements
+    assert q(A, qar.QAR_BF16, 1 << 17, 1 << 12, 64, B_, C, None) == qar.QAR_ERR_INVALID_ARG   # too many blocks
+    d = L.qar_dequantize_rows
+    assert d(A, C, 3, 100, 256, A + 8, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG        # out overlaps codes
+    r = L.qar_reduce_quantized_rows
+    assert r(_arr(A, B_), _arr(C, D), 2, 3, 100, 256, 0x50000, 0x60000, 0x70001, qar.QAR_BF16, None) == \
+        qar.QAR_ERR_MISALIGNED
+    g = L.qar_ring_step_rows
+    assert g(A, C, B_, qar.QAR_BF16, 3, 100, 256, A, D, None) == qar.QAR_ERR_INVALID_ARG     # half in place
