@@ -268,6 +268,7 @@ def main() -> int:
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
+        result["row_bounded"] = rows_bench(qar, torch, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, np, w, host, sets[0], torch)
@@ -449,6 +450,39 @@ def pipelined_bench(qar, torch, synth, dev, skew):
     best = min(sweep, key=lambda x: x["avg_us"])
     return {"workload": w.description + ", reduce without out", "sweep": sweep,
             "best": {k: best[k] for k in ("nchunks", "nstreams", "avg_us", "GBps", "hbm_frac")}}
+
+
+def rows_bench(qar, torch, dev):
+    """Row-bounded blocks on a [8192, 2880] bf16 tensor (2880 = 11 blocks of
+    256 + a partial block of 64 per row), N=8: quantize and the fused reduce
+    with bf16 out through the general one-wavefront-per-block kernels."""
+    rows, row_len, B, N = 8192, 2880, 256, 8
+    n = rows * row_len
+    nb = qar.row_blocks(rows, row_len, B)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    xs = [torch.randn(rows, row_len, generator=g, device=dev).to(torch.bfloat16) for _ in range(N)]
+    q = [qar.qar_quantize_rows(x, B) for x in xs]
+    nsets = 3                                   # 3 x ~400 MB
+    sets = [([c.clone() for c, _ in q], [s.clone() for _, s in q], torch.empty(n, dtype=torch.int8, device=dev),
+             torch.empty(nb, dtype=torch.float32, device=dev), torch.empty(n, dtype=torch.bfloat16, device=dev),
+             xs[0].clone()) for _ in range(nsets)]
+    del q
+
+    def fq(i):
+        c, s, co, so, out, x = sets[i]
+        qar.qar_quantize_rows(x, B, c[0], s[0])
+
+    def fr(i):
+        c, s, co, so, out, x = sets[i]
+        qar.qar_reduce_quantized_rows(c, s, rows, row_len, B, co, so, out=out)
+    qbytes = n + 4 * nb
+    res = {"shape": f"N={N} x [{rows}, {row_len}] bf16, block {B} (partial last block of 64 per row)",
+           "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 50)),
+           "reduce_fused_bf16_out": _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fr, nsets, 50))}
+    del sets, xs
+    torch.cuda.empty_cache()
+    return res
 
 
 def allreduce_bench(qar, torch, synth, dev):

@@ -420,6 +420,7 @@ qar_status qar_quantize_rows(const void* x, qar_dtype dtype, size_t rows, size_t
     const Range xi = range(x, sh.n * dtype_bytes(dtype)), co = range(codes, sh.n), so = range(scales, sh.nblocks * 4);
     if (overlap(xi, co) || overlap(xi, so) || overlap(co, so)) return QAR_ERR_INVALID_ARG;
     qar::RowsCall c = rows_call(qar::kRowsQuantize, sh, block);
+    c.vector = sh.row_len % 16 == 0 && aligned(x, 16) && aligned(codes, 16);
     c.kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
     c.x = x;
     c.codes_out = codes;
@@ -442,6 +443,7 @@ qar_status qar_dequantize_rows(const int8_t* codes, const float* scales, size_t 
                 oo = range(out, sh.n * dtype_bytes(out_dtype));
     if (overlap(oo, ci) || overlap(oo, si)) return QAR_ERR_INVALID_ARG;
     qar::RowsCall c = rows_call(qar::kRowsDequantize, sh, block);
+    c.vector = sh.row_len % 16 == 0 && aligned(codes, 16) && aligned(out, 16);
     c.kind = out_dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
     c.codes_in = codes;
     c.scales_in = scales;
@@ -489,6 +491,8 @@ qar_status qar_reduce_quantized_rows(const int8_t* const* codes, const float* co
         c.rp.scales[r] = scales[r];
     }
     if (same_codes != same_scales) return QAR_ERR_INVALID_ARG;
+    c.vector = sh.row_len % 16 == 0 && aligned(codes_out, 16) && (!out || aligned(out, 16));
+    for (uint32_t r = 0; c.vector && r < nranks; ++r) c.vector = aligned(codes[r], 16);
     c.kind = (out && out_dtype == QAR_F32) ? qar::kInF32 : qar::kInBF16;
     c.nranks = (int)nranks;
     c.codes_out = codes_out;
@@ -518,6 +522,7 @@ qar_status qar_ring_step_rows(const int8_t* codes_in, const float* scales_in, co
         return QAR_ERR_INVALID_ARG;
     if ((co.lo == ci.lo) != (so.lo == si.lo)) return QAR_ERR_INVALID_ARG;
     qar::RowsCall c = rows_call(qar::kRowsRingStep, sh, block);
+    c.vector = sh.row_len % 16 == 0 && aligned(codes_in, 16) && aligned(codes_out, 16) && aligned(local, 16);
     c.kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
     c.x = local;
     c.codes_in = codes_in;

@@ -18,26 +18,84 @@
 namespace qar {
 
 // ---------------------------------------------------------------------------
+// where each lane works
+//
+// Global lane g owns 16 consecutive elements starting at e0, inside block
+// blk; the B/16 lanes of a block are adjacent (one DPP row or part of one).
+//   FlatLanes: blocks tile the buffer: e0 = 16 g, blk = e0 / B.
+//   RowLanes:  row-bounded blocks of a [rows, row_len] tensor with
+//              row_len % 16 == 0: block blk = (row r, k-th block of the
+//              row) starts at r * row_len + k * B; lanes past the end of a
+//              row's partial last block are invalid and contribute nothing
+//              to the block's absmax.
+// Invalid lanes read element 0 (any finite value) and store nothing.
+struct LaneAt {
+    size_t e0, blk;
+    bool valid, leads; // leads: first lane of its block (writes the scale)
+};
+
+template <int B>
+struct FlatLanes {
+    size_t n;
+    static constexpr bool kContiguous = true; // a wave covers 1024 consecutive elements
+    static constexpr bool kPartialBlocks = false;
+    __device__ __forceinline__ LaneAt at(size_t g) const {
+        LaneAt a;
+        a.e0 = g * kLaneElems;
+        a.valid = a.e0 < n;
+        a.blk = a.e0 / B;
+        a.leads = a.e0 % B == 0;
+        return a;
+    }
+};
+
+template <int B>
+struct RowLanes {
+    size_t row_len, nblocks;
+    uint32_t per_row; // blocks per row
+    static constexpr bool kContiguous = false;
+    static constexpr bool kPartialBlocks = true;
+    __device__ __forceinline__ LaneAt at(size_t g) const {
+        constexpr uint32_t L = B / kLaneElems;
+        LaneAt a;
+        a.blk = g / L;
+        const uint32_t j = (uint32_t)(g % L);
+        const uint32_t b32 = (uint32_t)a.blk; // nblocks < 2^26
+        const uint32_t r = b32 / per_row, k = b32 - r * per_row;
+        const size_t col = (size_t)k * B + (size_t)j * kLaneElems;
+        a.e0 = (size_t)r * row_len + col;
+        a.valid = a.blk < nblocks && col < row_len;
+        a.leads = j == 0;
+        return a;
+    }
+};
+
+// absmax over a lane's values, zero for an invalid lane of a partial block
+template <typename Lanes>
+__device__ __forceinline__ float masked_absmax(const float (&v)[kLaneElems], bool valid) {
+    const float m = lane_absmax(v);
+    if constexpr (Lanes::kPartialBlocks) return valid ? m : 0.0f;
+    return m;
+}
+
+// ---------------------------------------------------------------------------
 // quantize: x (bf16 or fp32) -> codes, scales
 
-template <int B, typename In>
-__global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x, size_t n,
+template <int B, typename In, typename Lanes>
+__global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x, Lanes lanes,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
                                                        uint32_t ntiles) {
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
-        const bool valid = e0 < n;
-        // Lanes past the end read element 0 instead: blocks never straddle
-        // the end, so their (discarded) results cannot touch a valid block.
-        const size_t ld = valid ? e0 : 0;
+        const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
+        const size_t ld = a.valid ? a.e0 : 0;
         float v[kLaneElems];
         load16(x + ld, v);
-        const float s = block_max<B>(lane_absmax(v)) / 127.0f;
+        const float s = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / 127.0f;
         const uint4 q = quantize16(v, s);
-        if (valid) {
-            store_b128(codes + e0, q);
-            if (e0 % B == 0) scales[e0 / B] = s;
+        if (a.valid) {
+            store_b128(codes + a.e0, q);
+            if (a.leads) scales[a.blk] = s;
         }
     }
 }
@@ -94,18 +152,18 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int B, int OUT>
-__global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, size_t n,
+template <int B, int OUT, typename Lanes>
+__global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
                                                      int8_t* codes_out, float* scales_out,
                                                      void* __restrict__ out, uint32_t ntiles) {
     constexpr int G = 8; // ranks whose loads are in flight together
-    __shared__ uint4 lds_codes[OUT != kOutNone ? kThreads : 1];
-    __shared__ float lds_scales[OUT != kOutNone ? kThreads * kLaneElems / B : 1];
+    constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
+    __shared__ uint4 lds_codes[kStaged ? kThreads : 1];
+    __shared__ float lds_scales[kStaged ? kThreads * kLaneElems / B : 1];
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
-        const bool valid = e0 < n;
-        const size_t ld = valid ? e0 : 0; // see k_quantize
-        const size_t blk = ld / B;
+        const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
+        const size_t ld = a.valid ? a.e0 : 0;
+        const size_t blk = a.valid ? a.blk : 0;
         float acc[kLaneElems];
         for (int g = 0; g < nranks; g += G) {
             uint4 q[G];
@@ -132,16 +190,28 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, si
                 }
             }
         }
-        const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
-        const uint4 qo = quantize16(acc, so);
-        if (valid) {
-            store_b128(codes_out + e0, qo);
-            if (e0 % B == 0) scales_out[blk] = so;
+        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / 127.0f;
+        uint32_t w[kLaneElems];
+        const uint4 qo = quantize16(acc, so, w);
+        if (a.valid) {
+            store_b128(codes_out + a.e0, qo);
+            if (a.leads) scales_out[a.blk] = so;
         }
-        if constexpr (OUT != kOutNone) {
+        if constexpr (kStaged) {
             const int wave = threadIdx.x / 64;
-            store_dequantized_tile<B, OUT>(qo, so, e0, n, out, lds_codes + wave * 64,
+            store_dequantized_tile<B, OUT>(qo, so, a.e0, lanes.n, out, lds_codes + wave * 64,
                                            lds_scales + wave * (64 * kLaneElems / B));
+        } else if constexpr (OUT != kOutNone) {
+            // row-bounded blocks: a wave's elements are not one contiguous
+            // range, so each lane stores its own 16 values
+            if (a.valid) {
+                float y[kLaneElems];
+                dequantize_words(w, so, y);
+                if constexpr (OUT == kOutBF16)
+                    store16(static_cast<uint16_t*>(out) + a.e0, y);
+                else
+                    store16(static_cast<float*>(out) + a.e0, y);
+            }
         }
     }
 }
@@ -149,16 +219,15 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, si
 // ---------------------------------------------------------------------------
 // ring step: dequantize incoming + add local (bf16/fp32) + requantize
 
-template <int B, typename In>
+template <int B, typename In, typename Lanes>
 __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, const float* scales_in,
-                                                        const In* __restrict__ local, size_t n,
+                                                        const In* __restrict__ local, Lanes lanes,
                                                         int8_t* codes_out, float* scales_out,
                                                         uint32_t ntiles) {
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * kLaneElems;
-        const bool valid = e0 < n;
-        const size_t ld = valid ? e0 : 0; // see k_quantize
-        const size_t blk = ld / B;
+        const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
+        const size_t ld = a.valid ? a.e0 : 0;
+        const size_t blk = a.valid ? a.blk : 0;
         float acc[kLaneElems];
         {
             const uint4 q = load_b128(codes_in + ld);
@@ -169,11 +238,11 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
 #pragma unroll
             for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + x[i];
         }
-        const float so = block_max<B>(lane_absmax(acc)) / 127.0f;
+        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / 127.0f;
         const uint4 qo = quantize16(acc, so);
-        if (valid) {
-            store_b128(codes_out + e0, qo);
-            if (e0 % B == 0) scales_out[blk] = so;
+        if (a.valid) {
+            store_b128(codes_out + a.e0, qo);
+            if (a.leads) scales_out[a.blk] = so;
         }
     }
 }
@@ -216,6 +285,22 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
             }
             store_b128(out + e, o);
         }
+    }
+}
+
+// Row-bounded blocks with row_len % 16 == 0: each lane dequantizes its own
+// 16 codes.
+template <int B, typename Out>
+__global__ __launch_bounds__(kThreads) void k_dequantize_lanes(const int8_t* __restrict__ codes,
+                                                               const float* __restrict__ scales,
+                                                               RowLanes<B> lanes, Out* __restrict__ out,
+                                                               uint32_t ntiles) {
+    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+        const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
+        if (!a.valid) continue;
+        float y[kLaneElems];
+        dequantize16(load_b128(codes + a.e0), scales[a.blk], y);
+        store16(out + a.e0, y);
     }
 }
 
@@ -502,46 +587,44 @@ Grid grid_for(size_t n) {
     return g;
 }
 
-template <int B>
-hipError_t quantize_b(const void* x, int in_kind, size_t n, int8_t* codes, float* scales, hipStream_t st) {
-    const Grid g = grid_for(n);
+Grid grid_lanes(size_t lanes) { return grid_for(lanes * kLaneElems); }
+
+template <int B, typename Lanes>
+hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* codes, float* scales,
+                      hipStream_t st) {
     if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_quantize<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(x), n, codes, scales, g.ntiles);
+        hipLaunchKernelGGL((k_quantize<B, uint16_t, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st,
+                           static_cast<const uint16_t*>(x), lanes, codes, scales, g.ntiles);
     else
-        hipLaunchKernelGGL((k_quantize<B, float>), dim3(g.blocks), dim3(kThreads), 0, st,
-                           static_cast<const float*>(x), n, codes, scales, g.ntiles);
+        hipLaunchKernelGGL((k_quantize<B, float, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st,
+                           static_cast<const float*>(x), lanes, codes, scales, g.ntiles);
     return hipGetLastError();
 }
 
-template <int B>
-hipError_t reduce_b(const RankPtrs& rp, int nranks, size_t n, int8_t* codes_out, float* scales_out,
+template <int B, typename Lanes>
+hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t* codes_out, float* scales_out,
                     void* out, int out_kind, hipStream_t st) {
-    const Grid g = grid_for(n);
     if (out_kind == kOutBF16)
-        hipLaunchKernelGGL((k_reduce<B, kOutBF16>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
-                           codes_out, scales_out, out, g.ntiles);
+        hipLaunchKernelGGL((k_reduce<B, kOutBF16, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+                           lanes, codes_out, scales_out, out, g.ntiles);
     else if (out_kind == kOutF32)
-        hipLaunchKernelGGL((k_reduce<B, kOutF32>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
-                           codes_out, scales_out, out, g.ntiles);
+        hipLaunchKernelGGL((k_reduce<B, kOutF32, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+                           lanes, codes_out, scales_out, out, g.ntiles);
     else
-        hipLaunchKernelGGL((k_reduce<B, kOutNone>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks, n,
-                           codes_out, scales_out, out, g.ntiles);
+        hipLaunchKernelGGL((k_reduce<B, kOutNone, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+                           lanes, codes_out, scales_out, out, g.ntiles);
     return hipGetLastError();
 }
 
-template <int B>
-hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
-                  size_t n, int8_t* codes_out, float* scales_out, hipStream_t st) {
-    const Grid g = grid_for(n);
+template <int B, typename Lanes>
+hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind, Lanes lanes,
+                  Grid g, int8_t* codes_out, float* scales_out, hipStream_t st) {
     if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_ring_step<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
-                           scales_in, static_cast<const uint16_t*>(local), n, codes_out, scales_out,
-                           g.ntiles);
+        hipLaunchKernelGGL((k_ring_step<B, uint16_t, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+                           scales_in, static_cast<const uint16_t*>(local), lanes, codes_out, scales_out, g.ntiles);
     else
-        hipLaunchKernelGGL((k_ring_step<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
-                           scales_in, static_cast<const float*>(local), n, codes_out, scales_out,
-                           g.ntiles);
+        hipLaunchKernelGGL((k_ring_step<B, float, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+                           scales_in, static_cast<const float*>(local), lanes, codes_out, scales_out, g.ntiles);
     return hipGetLastError();
 }
 
@@ -558,11 +641,53 @@ hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void
     return hipGetLastError();
 }
 
+template <int B>
+RowLanes<B> row_lanes(const RowsCall& c, size_t& nlanes) {
+    RowLanes<B> l;
+    l.row_len = c.row_len;
+    l.per_row = (uint32_t)((c.row_len + B - 1) / B);
+    l.nblocks = c.rows * l.per_row;
+    nlanes = l.nblocks * (B / kLaneElems);
+    return l;
+}
+
+// row-bounded blocks, row_len % 16 == 0: the vector kernels on RowLanes
+template <int B>
+hipError_t rows_vector(const RowsCall& c, hipStream_t st) {
+    size_t nlanes = 0;
+    const RowLanes<B> l = row_lanes<B>(c, nlanes);
+    const Grid g = grid_lanes(nlanes);
+    switch (c.op) {
+    case kRowsQuantize:
+        return quantize_b<B>(c.x, c.kind, l, g, c.codes_out, c.scales_out, st);
+    case kRowsReduce:
+        return reduce_b<B>(c.rp, c.nranks, l, g, c.codes_out, c.scales_out, c.out,
+                           c.out ? (c.kind == kInBF16 ? kOutBF16 : kOutF32) : kOutNone, st);
+    case kRowsRingStep:
+        return ring_b<B>(c.codes_in, c.scales_in, c.x, c.kind, l, g, c.codes_out, c.scales_out, st);
+    default:
+        if (c.kind == kInBF16)
+            hipLaunchKernelGGL((k_dequantize_lanes<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st,
+                               c.codes_in, c.scales_in, l, static_cast<uint16_t*>(c.out), g.ntiles);
+        else
+            hipLaunchKernelGGL((k_dequantize_lanes<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, c.codes_in,
+                               c.scales_in, l, static_cast<float*>(c.out), g.ntiles);
+        return hipGetLastError();
+    }
+}
+
 uint32_t row_grid(size_t nblocks) { return (uint32_t)((nblocks + kThreads / 64 - 1) / (kThreads / 64)); }
 
 } // namespace
 
 hipError_t launch_rows(const RowsCall& c, hipStream_t st) {
+    if (c.vector) {
+        switch (c.block) {
+        case 64: return rows_vector<64>(c, st);
+        case 128: return rows_vector<128>(c, st);
+        default: return rows_vector<256>(c, st);
+        }
+    }
     RowMap map;
     map.rows = c.rows;
     map.row_len = c.row_len;
@@ -621,28 +746,33 @@ hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, 
 
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
                            hipStream_t st) {
+    const Grid g = grid_for(n);
     switch (block) {
-    case 64: return quantize_b<64>(x, in_kind, n, codes, scales, st);
-    case 128: return quantize_b<128>(x, in_kind, n, codes, scales, st);
-    default: return quantize_b<256>(x, in_kind, n, codes, scales, st);
+    case 64: return quantize_b<64>(x, in_kind, FlatLanes<64>{n}, g, codes, scales, st);
+    case 128: return quantize_b<128>(x, in_kind, FlatLanes<128>{n}, g, codes, scales, st);
+    default: return quantize_b<256>(x, in_kind, FlatLanes<256>{n}, g, codes, scales, st);
     }
 }
 
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
                          float* scales_out, void* out, int out_kind, hipStream_t st) {
+    const Grid g = grid_for(n);
     switch (block) {
-    case 64: return reduce_b<64>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
-    case 128: return reduce_b<128>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
-    default: return reduce_b<256>(rp, nranks, n, codes_out, scales_out, out, out_kind, st);
+    case 64: return reduce_b<64>(rp, nranks, FlatLanes<64>{n}, g, codes_out, scales_out, out, out_kind, st);
+    case 128: return reduce_b<128>(rp, nranks, FlatLanes<128>{n}, g, codes_out, scales_out, out, out_kind, st);
+    default: return reduce_b<256>(rp, nranks, FlatLanes<256>{n}, g, codes_out, scales_out, out, out_kind, st);
     }
 }
 
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
                             size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st) {
+    const Grid g = grid_for(n);
     switch (block) {
-    case 64: return ring_b<64>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
-    case 128: return ring_b<128>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
-    default: return ring_b<256>(codes_in, scales_in, local, in_kind, n, codes_out, scales_out, st);
+    case 64: return ring_b<64>(codes_in, scales_in, local, in_kind, FlatLanes<64>{n}, g, codes_out, scales_out, st);
+    case 128:
+        return ring_b<128>(codes_in, scales_in, local, in_kind, FlatLanes<128>{n}, g, codes_out, scales_out, st);
+    default:
+        return ring_b<256>(codes_in, scales_in, local, in_kind, FlatLanes<256>{n}, g, codes_out, scales_out, st);
     }
 }
 

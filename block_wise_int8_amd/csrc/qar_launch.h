@@ -28,6 +28,7 @@ struct PlainPtrs {
 enum : int { kRowsQuantize = 0, kRowsDequantize = 1, kRowsReduce = 2, kRowsRingStep = 3 };
 struct RowsCall {
     int op;
+    bool vector;              // row_len % 16 == 0 and 16-byte aligned: the vector kernels
     int kind;                 // element type of x / out (kInBF16 or kInF32)
     size_t rows, row_len;
     int block;

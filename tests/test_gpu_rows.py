@@ -119,3 +119,19 @@ def test_rows_on_the_flat_path_equal_flat_calls():
     c2, s2 = qar.qar_quantize_blocks(x, block)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_rows_unaligned_pointers_take_the_general_path(oracle_lib):
+    """row_len % 16 == 0 but the data starts 2 bytes into an allocation:
+    the element-wise kernels run, with the same results."""
+    rows, row_len, block = 7, 2880, 256
+    x = _data(99, rows, row_len, "bf16")
+    base = torch.empty(rows * row_len + 8, dtype=torch.bfloat16, device="cuda:0")
+    view = base[1:1 + rows * row_len]
+    view.copy_(to_dev(x.reshape(-1)))
+    codes = torch.empty(rows * row_len + 16, dtype=torch.int8, device="cuda:0")[3:3 + rows * row_len]
+    c, s = qar.qar_quantize_rows(view.view(rows, row_len), block, codes=codes)
+    torch.cuda.synchronize()
+    wc, ws = _oracle_quantize_rows(oracle_lib, x, block)
+    assert_same_codes(to_host(c), wc, "codes")
+    assert_same_f32(to_host(s), ws, "scales")
