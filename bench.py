@@ -2,18 +2,19 @@
 AllReduce (EQuARX) on the outlier workload: N=8 ranks x 16,777,216 bf16
 elements ~ N(0,1) with 0.1% N(0,1)*50 outliers, blocks of 256.
 
-One step = the whole per-GPU path over one batch:
-  1. quantize this GPU's own bf16 buffer (absmax -> scale -> int8 codes);
-  2. one fused kernel over the N quantized contributions (this rank's and
-     the N-1 peers', resident in HBM): dequantize, fp32 sum in rank order,
-     requantize, and dequantize the result back to bf16.
-The peers' codes are produced by the same quantize kernel before timing.
+One step = the whole per-GPU path over one batch, in one kernel
+(qar_quantize_reduce): quantize this GPU's own bf16 buffer (absmax -> scale
+-> int8 codes, written out for the peers), dequantize it and the N-1 peers'
+quantized contributions (resident in HBM), fp32 sum in rank order,
+requantize, and dequantize the result back to bf16.  The peers' codes are
+produced by the quantize kernel before timing.  The same step as two
+kernels (quantize, then the plain reduce) is reported beside it.
 Buffer sets rotate every step (footprint > 1 GiB) so the 256 MB Infinity
 Cache cannot serve a step from the previous one's data: inputs are resident
 in HBM, not in cache, when a step starts.
 
 Prints ONE JSON line.  value = bf16 payload bytes (N * n * 2) per step /
-step time.  roofline = the dominant kernel (the fused reduce) against the
+step time.  roofline = the step's kernel against the
 MI355X HBM peak; cpu_baseline = the CPU oracle on the same inputs.
 Extra keys report each kernel's own time, the reduce without the fused
 dequantize (N*qbytes read + qbytes written) and a ring step.
@@ -33,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
-DOMINANT = "k_reduce"
+DOMINANT = "k_quantize_reduce"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_wise_int8_amd", "csrc", f)
                   for f in ("qar_kernels.hip", "qar_device.h")]
@@ -47,10 +48,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def counters_path(workload_key: str) -> str:
+    return os.path.join(PROFILES, f"{DOMINANT}_{workload_key}_counters.json")
+
+
 def measured_traffic(workload_key: str):
     """HBM bytes per launch of the dominant kernel from the committed
     counter summary, if it was taken on the current kernel sources."""
-    path = os.path.join(PROFILES, f"reduce_{workload_key}_counters.json")
+    path = counters_path(workload_key)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -75,11 +80,68 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip the reduce-only and ring-step lines")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run 8 device-to-device copies of this many MiB (counter calibration) and exit")
+    p.add_argument("--summarize-counters", metavar="DIR", default=None,
+                   help="no GPU: read the rocprofv3 --pmc CSVs of the four counter passes under DIR "
+                        "(pmc_copy_fetch, pmc_copy_write, pmc_fetch, pmc_write) and write the traffic summary "
+                        "of the step's kernels under profiles/")
     return p.parse_args()
+
+
+# (name in the trace, algorithmic read bytes, algorithmic write bytes) for
+# the outlier workload's kernels; N ranks, n elements, block B, bf16 in/out
+def _counter_kernels(N, n, B):
+    qb = n + 4 * (n // B)
+    return [("k_quantize_reduce<", 2 * n + (N - 1) * qb, 2 * qb + 2 * n),
+            ("k_quantize<", 2 * n, qb),
+            ("k_reduce<", N * qb, qb + 2 * n)]
+
+
+def summarize_counters(d: str) -> int:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's kernels,
+    scaled by what the same counters read for a plain 1 GiB device copy."""
+    import csv
+    import statistics
+
+    def mean_kib(sub, match):
+        files = [os.path.join(r, f) for r, _, fs in os.walk(os.path.join(d, sub)) for f in fs
+                 if f.endswith("counter_collection.csv")]
+        v = [float(r["Counter_Value"]) for p in files for r in csv.DictReader(open(p)) if match in r["Kernel_Name"]]
+        if not v:
+            raise SystemExit(f"no dispatch of {match} under {d}/{sub}")
+        return statistics.mean(v), len(v)
+
+    copy_kib = 1 << 20
+    cf, _ = mean_kib("pmc_copy_fetch", "copyBuffer")
+    cw, _ = mean_kib("pmc_copy_write", "copyBuffer")
+    ff, fw = copy_kib / cf, copy_kib / cw
+    from block_wise_int8_amd import synth
+    w = synth.WORKLOADS["outliers"]
+    rows = {}
+    for name, alg_r, alg_w in _counter_kernels(w.nranks, w.n, w.block):
+        f, nd = mean_kib("pmc_fetch", name)
+        wr, _ = mean_kib("pmc_write", name)
+        rd, wb = int(f * ff * 1024), int(wr * fw * 1024)
+        rows[name.rstrip("<")] = {"dispatches": nd, "fetch_kib_raw_mean": round(f, 2), "write_kib_raw_mean": round(wr, 2),
+                                  "hbm_read_bytes": rd, "hbm_write_bytes": wb, "algorithmic_read_bytes": alg_r,
+                                  "algorithmic_write_bytes": alg_w,
+                                  "traffic_over_algorithmic": round((rd + wb) / (alg_r + alg_w), 4)}
+    top = rows[DOMINANT]
+    rec = {"kernel": DOMINANT, "workload": f"{w.key}: {w.description}",
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": round(cf, 2), "write_kib_raw": round(cw, 2),
+                           "fetch_factor": round(ff, 5), "write_factor": round(fw, 5)},
+           "hbm_bytes_per_launch": top["hbm_read_bytes"] + top["hbm_write_bytes"],
+           "kernels": rows}
+    with open(counters_path(w.key), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+    return 0
 
 
 def main() -> int:
     args = parse()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} "
@@ -170,10 +232,12 @@ def main() -> int:
         qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"],
                                  out=st["out"], stream=stream)
 
+    def fused_step(st):
+        qar.qar_quantize_reduce(st["x"], 0, st["codes"], st["scales"], B, st["codes_out"], st["scales_out"],
+                                out=st["out"], stream=stream)
+
     def step(i):
-        st = sets[i % len(sets)]
-        quantize_own(st)
-        reduce_fused(st)
+        fused_step(sets[i % len(sets)])
 
     for i in range(args.warmup):
         step(i)
@@ -192,30 +256,33 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     # each kernel of the step on its own: R launches back to back over the
-    # rotated sets, one event pair around them (events between kernels
-    # would add their own overhead to every launch)
+    # rotated sets, events only at 5 segment boundaries (events between
+    # kernels would add their own overhead to every launch)
     def per_launch_us(fn, reps):
         for i in range(3):
             fn(sets[i % len(sets)])
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(reps):
-            fn(sets[i % len(sets)])
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3
+        return _segmented_us(torch, lambda i: fn(sets[i % len(sets)]), reps)
 
     reps = max(args.steps, 50)
+    f_us = per_launch_us(fused_step, reps)
     q_us = per_launch_us(quantize_own, reps)
     r_us = per_launch_us(reduce_fused, reps)
 
+    def two_kernels(st):
+        quantize_own(st)
+        reduce_fused(st)
+    two_us = per_launch_us(two_kernels, reps)
+
     payload = N * n * 2
     value = payload / (ms_per_step * 1e-3) / 1e9
+    in_bytes = n * (2 if w.dtype == "bf16" else 4)
     out_bytes = n * (2 if out_dtype == torch.bfloat16 else 4)
     reduce_bytes = N * qbytes + qbytes + out_bytes          # algorithmic, per launch
-    quant_bytes = n * (2 if w.dtype == "bf16" else 4) + qbytes
-    achieved = reduce_bytes / (r_us * 1e-6) / 1e9
+    quant_bytes = in_bytes + qbytes
+    # own input read + N-1 peers' codes/scales read + own codes/scales,
+    # result codes/scales and the dequantized result written
+    fused_bytes = in_bytes + (N - 1) * qbytes + 2 * qbytes + out_bytes
+    achieved = fused_bytes / (f_us * 1e-6) / 1e9
 
     result = {
         "metric": "GB/s of bf16 payload reduced per GPU and % of HBM peak, fused quantized reduce",
@@ -233,7 +300,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.key}: {w.description}",
             "nranks": N, "elements_per_rank": n, "block": B, "input_dtype": w.dtype,
-            "step": "quantize own buffer + fused reduce/requantize/dequantize of N contributions",
+            "step": "one kernel: quantize own buffer + reduce/requantize/dequantize of N contributions",
             "buffer_sets": args.sets, "footprint_bytes": set_bytes * args.sets,
             "rank_stride_bytes": stride if args.skew >= 0 else None,
             "parallelism": "one GPU's share",
@@ -246,16 +313,21 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.key),
-            "algorithmic_bytes_per_launch": reduce_bytes,
-            "avg_launch_us": round(r_us, 3),
-            "timing": f"{reps} back-to-back launches over the rotated sets, one HIP event pair",
+            "algorithmic_bytes_per_launch": fused_bytes,
+            "avg_launch_us": round(f_us, 3),
+            "timing": f"{reps} back-to-back launches over the rotated sets, median of 5 event-bracketed segments",
         },
         "kernels": {
+            "k_quantize_reduce (the step)": {"avg_us": round(f_us, 3), "bytes": fused_bytes,
+                                             "GBps": round(achieved, 1)},
             "k_quantize": {"avg_us": round(q_us, 3), "bytes": quant_bytes,
                            "GBps": round(quant_bytes / (q_us * 1e-6) / 1e9, 1)},
-            "k_reduce (fused bf16 out)": {"avg_us": round(r_us, 3), "bytes": reduce_bytes,
-                                          "GBps": round(achieved, 1)},
+            "k_reduce (bf16 out)": {"avg_us": round(r_us, 3), "bytes": reduce_bytes,
+                                    "GBps": round(reduce_bytes / (r_us * 1e-6) / 1e9, 1)},
         },
+        "two_kernel_step": {"avg_us": round(two_us, 3), "bytes": quant_bytes + reduce_bytes,
+                            "payload_GBps": round(payload / (two_us * 1e-6) / 1e9, 1),
+                            "note": "the same step as k_quantize then k_reduce, back to back"},
         "input_generation_s": round(gen_s, 2),
     }
 
@@ -263,7 +335,7 @@ def main() -> int:
         result["reduce_only"] = reduce_only(args, qar, torch, sets, B, N, n, qbytes)
         result["dequantize"] = dequantize_bench(qar, torch, sets, B, n, qbytes)
         result["unquantized_comparator"] = comparator_bench(qar, torch, synth, w, dev, args.skew,
-                                                            result["reduce_only"]["avg_us"], r_us, q_us)
+                                                            result["reduce_only"]["avg_us"], f_us)
         result["ring_step"] = ring_bench(qar, torch, np, synth, dev)
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
@@ -282,18 +354,11 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
     N*qbytes, writes qbytes."""
     stream = torch.cuda.current_stream()
     reps = max(args.steps, 20)
-    for i in range(5):
+
+    def fn(i):
         st = sets[i % len(sets)]
         qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"], stream=stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(reps):
-        st = sets[i % len(sets)]
-        qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"], stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+    us = _loop_us(torch, fn, len(sets), reps, warmup=5)
     nbytes = (N + 1) * qbytes
     return {"avg_us": round(us, 3), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
@@ -302,20 +367,34 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
             "note": "back-to-back launches over rotated buffer sets, out=NULL"}
 
 
-def _loop_us(torch, fn, count, reps, warmup=3):
-    """Average time of fn(i) over reps back-to-back launches (i cycles over
-    `count` buffer sets), one HIP event pair."""
+def _segmented_us(torch, fn, reps, segments=5):
+    """fn(i) for i in range(reps) back to back on the current stream, with
+    an event at each of `segments` boundaries (no synchronisation between
+    them).  Returns the median over segments of the average time per call,
+    so a host-side pause that lets the GPU idle in one segment does not
+    count."""
     stream = torch.cuda.current_stream()
+    per = max(1, reps // segments)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(segments + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    i = 0
+    for k in range(segments):
+        for _ in range(per):
+            fn(i)
+            i += 1
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    seg = sorted(ev[k].elapsed_time(ev[k + 1]) / per * 1e3 for k in range(segments))
+    return seg[len(seg) // 2]
+
+
+def _loop_us(torch, fn, count, reps, warmup=3):
+    """Time per fn(i) over reps back-to-back launches (i cycles over
+    `count` buffer sets), median of 5 event-bracketed segments."""
     for i in range(warmup):
         fn(i % count)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(reps):
-        fn(i % count)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps * 1e3
+    return _segmented_us(torch, lambda i: fn(i % count), reps)
 
 
 def _rate(nbytes, us):
@@ -348,7 +427,7 @@ def dequantize_bench(qar, torch, sets, B, n, qbytes):
     return _rate(qbytes + 2 * n, _loop_us(torch, fn, len(sets), 100))
 
 
-def comparator_bench(qar, torch, synth, w, dev, skew, reduce_only_us, reduce_out_us, quant_us):
+def comparator_bench(qar, torch, synth, w, dev, skew, reduce_only_us, step_us):
     """The unquantized N-way bf16 reduce (rank-order fp32 sum, bf16 out) on
     the same shape: reads N*2n, writes 2n.  Ratios to the quantized path
     are the one-GPU analog of the pages' speed-up over a BF16 AllReduce."""
@@ -366,9 +445,10 @@ def comparator_bench(qar, torch, synth, w, dev, skew, reduce_only_us, reduce_out
     us = _loop_us(torch, fn, nsets, 50)
     res = _rate(N * n * 2 + n * 2, us)
     res["speedup_of_quantized_reduce"] = round(us / reduce_only_us, 3)
-    res["speedup_of_quantized_step"] = round(us / (quant_us + reduce_out_us), 3)
-    res["note"] = ("speedup_of_quantized_reduce = this time / fused quantized reduce time (same N, n); "
-                   "speedup_of_quantized_step = this time / (quantize own + fused reduce with bf16 out)")
+    res["speedup_of_quantized_step"] = round(us / step_us, 3)
+    res["note"] = ("speedup_of_quantized_reduce = this time / quantized reduce time (same N, n, no out); "
+                   "speedup_of_quantized_step = this time / the step (quantize own + reduce, bf16 out, "
+                   "one kernel)")
     del sets
     torch.cuda.empty_cache()
     return res
@@ -581,7 +661,9 @@ def cpu_baseline(args, np, w, host, set0, torch):
     dt = (time.perf_counter() - t0) / reps
     gpu_codes = set0["codes_out"].cpu().numpy()
     gpu_out = set0["out"].contiguous().view(torch.int16 if w.dtype == "bf16" else torch.int32).cpu().numpy()
-    same = bool(np.array_equal(gpu_codes, oc)) and bool(np.array_equal(gpu_out.view(y.dtype), y))
+    own_codes = set0["codes"][0].cpu().numpy()         # written by the step for the peers
+    same = (bool(np.array_equal(gpu_codes, oc)) and bool(np.array_equal(gpu_out.view(y.dtype), y))
+            and bool(np.array_equal(own_codes, c0)))
     return {"value": round(w.nranks * w.n * 2 / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole workload, {reps} repetitions of the step (quantize own buffer, reduce "
                       f"{w.nranks} ranks, dequantize); {dt:.3f} s per step on one host thread",

@@ -176,6 +176,44 @@ qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* 
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized");
 }
 
+qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
+                               float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                               int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                               void* stream) {
+    if (n == 0) return QAR_OK;
+    if (!x_own || !codes || !scales) return QAR_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
+    if (nranks == 0 || nranks > QAR_MAX_RANKS || own >= nranks) return QAR_ERR_INVALID_ARG;
+    qar_status st = check_reduce((const int8_t* const*)codes, (const float* const*)scales, nranks, n, block,
+                                 codes_out, scales_out, out, out_dtype);
+    if (st != QAR_OK) return st;
+    if (!aligned(x_own, 16)) return QAR_ERR_MISALIGNED;
+    const size_t nb = n / block;
+    // Written: rank own's codes and scales, the result (codes, scales, out).
+    // Each may overlap nothing else the call reads or writes.
+    Range w[5] = {range(codes[own], n), range(scales[own], nb * 4), range(codes_out, n),
+                  range(scales_out, nb * 4), out ? range(out, n * dtype_bytes(out_dtype)) : Range{0, 0}};
+    const Range xi = range(x_own, n * dtype_bytes(dtype));
+    for (int i = 0; i < 5; ++i)
+        if (overlap(w[i], xi)) return QAR_ERR_INVALID_ARG;
+    if (overlap(w[0], w[1])) return QAR_ERR_INVALID_ARG;
+    for (int i = 0; i < 2; ++i) {
+        for (int j = 2; j < 5; ++j)
+            if (overlap(w[i], w[j])) return QAR_ERR_INVALID_ARG;
+        for (uint32_t r = 0; r < nranks; ++r) {
+            if (r == own) continue;
+            if (overlap(w[i], range(codes[r], n)) || overlap(w[i], range(scales[r], nb * 4)))
+                return QAR_ERR_INVALID_ARG;
+        }
+    }
+    qar::RankPtrs rp;
+    fill_ranks(rp, (const int8_t* const*)codes, (const float* const*)scales, nranks, 0, 0);
+    const hipError_t e = qar::launch_quantize_reduce(
+        x_own, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, (int)own, rp, (int)nranks, n, (int)block,
+        codes[own], scales[own], codes_out, scales_out, out, out_kind(out, out_dtype), (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_quantize_reduce");
+}
+
 qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
                                           uint32_t nranks, size_t n, uint32_t block, int8_t* codes_out,
                                           float* scales_out, void* out, qar_dtype out_dtype,

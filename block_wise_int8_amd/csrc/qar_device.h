@@ -183,10 +183,24 @@ __device__ __forceinline__ void dequantize16(uint4 q, float s, float (&y)[kLaneE
 // ---------------------------------------------------------------------------
 // lane loads and stores of element data
 
-__device__ __forceinline__ void load16(const uint16_t* p, float (&v)[kLaneElems]) {
-    uint4 a = load_b128(p);
-    uint4 b = load_b128(p + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// A lane's 16 elements as loaded (32 bytes of bf16 or 64 of fp32), so a
+// caller can put other loads in flight before it converts them.
+template <typename In>
+struct Raw16 {
+    static constexpr int kWords = kLaneElems * (int)sizeof(In) / 16;
+    uint4 w[kWords];
+};
+
+template <typename In>
+__device__ __forceinline__ Raw16<In> load_raw16(const In* p) {
+    Raw16<In> r;
+#pragma unroll
+    for (int j = 0; j < Raw16<In>::kWords; ++j) r.w[j] = load_b128(p + j * (16 / sizeof(In)));
+    return r;
+}
+
+__device__ __forceinline__ void unpack16(const Raw16<uint16_t>& r, float (&v)[kLaneElems]) {
+    const uint32_t w[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         v[2 * j] = bf16_lo(w[j]);
@@ -194,15 +208,19 @@ __device__ __forceinline__ void load16(const uint16_t* p, float (&v)[kLaneElems]
     }
 }
 
-__device__ __forceinline__ void load16(const float* p, float (&v)[kLaneElems]) {
+__device__ __forceinline__ void unpack16(const Raw16<float>& r, float (&v)[kLaneElems]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint4 a = load_b128(p + 4 * j);
-        v[4 * j + 0] = __builtin_bit_cast(float, a.x);
-        v[4 * j + 1] = __builtin_bit_cast(float, a.y);
-        v[4 * j + 2] = __builtin_bit_cast(float, a.z);
-        v[4 * j + 3] = __builtin_bit_cast(float, a.w);
+        v[4 * j + 0] = __builtin_bit_cast(float, r.w[j].x);
+        v[4 * j + 1] = __builtin_bit_cast(float, r.w[j].y);
+        v[4 * j + 2] = __builtin_bit_cast(float, r.w[j].z);
+        v[4 * j + 3] = __builtin_bit_cast(float, r.w[j].w);
     }
+}
+
+template <typename In>
+__device__ __forceinline__ void load16(const In* p, float (&v)[kLaneElems]) {
+    unpack16(load_raw16(p), v);
 }
 
 __device__ __forceinline__ void store16(uint16_t* p, const float (&v)[kLaneElems]) {

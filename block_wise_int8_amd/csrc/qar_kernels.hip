@@ -12,6 +12,8 @@
 // reduction so the fp32 sum never leaves registers.  A workgroup walks tiles
 // of 4096 elements with a grid-stride loop (the grid is capped, the loop
 // covers any n).
+#include <type_traits>
+
 #include "qar_device.h"
 #include "qar_launch.h"
 
@@ -152,11 +154,17 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int B, int OUT, typename Lanes>
-__global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
-                                                     int8_t* codes_out, float* scales_out,
-                                                     void* __restrict__ out, uint32_t ntiles) {
+// The reduce over the tiles of one workgroup.  With OwnIn not void, rank
+// `own` is quantized from x_own in the same pass: its codes and scale are
+// written for the peers and the same register values enter the sum, so the
+// result equals a quantize followed by the plain reduce.
+template <int B, int OUT, typename Lanes, typename OwnIn>
+__device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
+                                             float* scales_out, void* __restrict__ out, uint32_t ntiles,
+                                             const OwnIn* __restrict__ x_own, int own,
+                                             int8_t* __restrict__ own_codes, float* __restrict__ own_scales) {
     constexpr int G = 8; // ranks whose loads are in flight together
+    constexpr bool kOwn = !std::is_void<OwnIn>::value;
     constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
     __shared__ uint4 lds_codes[kStaged ? kThreads : 1];
     __shared__ float lds_scales[kStaged ? kThreads * kLaneElems / B : 1];
@@ -164,15 +172,41 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, La
         const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
         const size_t ld = a.valid ? a.e0 : 0;
         const size_t blk = a.valid ? a.blk : 0;
+        // rank own's raw data is loaded first and converted while the first
+        // group's codes are in flight
+        using OwnRaw = Raw16<std::conditional_t<kOwn, OwnIn, uint16_t>>;
+        OwnRaw xr{};
+        if constexpr (kOwn) xr = load_raw16(x_own + ld);
+        uint4 q_own = make_uint4(0u, 0u, 0u, 0u);
+        float s_own = 0.0f;
         float acc[kLaneElems];
         for (int g = 0; g < nranks; g += G) {
             uint4 q[G];
             float s[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                if (g + j < nranks) {
+                if (g + j < nranks && !(kOwn && g + j == own)) {
                     q[j] = load_b128(rp.codes[g + j] + ld);
                     s[j] = rp.scales[g + j][blk];
+                }
+            }
+            if constexpr (kOwn) {
+                if (g == 0) {
+                    float v[kLaneElems];
+                    unpack16(xr, v);
+                    s_own = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / 127.0f;
+                    q_own = quantize16(v, s_own);
+                    if (a.valid) {
+                        store_b128(own_codes + a.e0, q_own);
+                        if (a.leads) own_scales[a.blk] = s_own;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (g + j == own) {
+                        q[j] = q_own;
+                        s[j] = s_own;
+                    }
                 }
             }
 #pragma unroll
@@ -214,6 +248,24 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, La
             }
         }
     }
+}
+
+template <int B, int OUT, typename Lanes>
+__global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
+                                                     int8_t* codes_out, float* scales_out,
+                                                     void* __restrict__ out, uint32_t ntiles) {
+    reduce_tiles<B, OUT, Lanes, void>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr, -1,
+                                      nullptr, nullptr);
+}
+
+template <int B, int OUT, typename In>
+__global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restrict__ x_own, int own,
+                                                              int8_t* own_codes, float* own_scales,
+                                                              RankPtrs rp, int nranks, FlatLanes<B> lanes,
+                                                              int8_t* codes_out, float* scales_out,
+                                                              void* __restrict__ out, uint32_t ntiles) {
+    reduce_tiles<B, OUT, FlatLanes<B>, In>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own, own,
+                                           own_codes, own_scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -589,6 +641,21 @@ Grid grid_for(size_t n) {
 
 Grid grid_lanes(size_t lanes) { return grid_for(lanes * kLaneElems); }
 
+template <typename T>
+struct TypeTag {
+    using type = T;
+};
+
+// calls f(std::integral_constant<int, B>) for the supported block sizes
+template <typename F>
+hipError_t dispatch_block(int block, F&& f) {
+    switch (block) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    default: return f(std::integral_constant<int, 256>{});
+    }
+}
+
 template <int B, typename Lanes>
 hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* codes, float* scales,
                       hipStream_t st) {
@@ -762,6 +829,36 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
     case 128: return reduce_b<128>(rp, nranks, FlatLanes<128>{n}, g, codes_out, scales_out, out, out_kind, st);
     default: return reduce_b<256>(rp, nranks, FlatLanes<256>{n}, g, codes_out, scales_out, out, out_kind, st);
     }
+}
+
+hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
+                                  size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
+                                  float* scales_out, void* out, int out_kind, hipStream_t st) {
+    const Grid g = grid_for(n);
+    return dispatch_block(block, [&](auto bc) {
+        constexpr int B = decltype(bc)::value;
+        const FlatLanes<B> lanes{n};
+        auto go = [&](auto oc, auto in_tag) {
+            constexpr int OUT = decltype(oc)::value;
+            using In = typename decltype(in_tag)::type;
+            hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In>), dim3(g.blocks), dim3(kThreads), 0, st,
+                               static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
+                               codes_out, scales_out, out, g.ntiles);
+        };
+        auto with_in = [&](auto oc) {
+            if (in_kind == kInBF16)
+                go(oc, TypeTag<uint16_t>{});
+            else
+                go(oc, TypeTag<float>{});
+        };
+        if (out_kind == kOutBF16)
+            with_in(std::integral_constant<int, kOutBF16>{});
+        else if (out_kind == kOutF32)
+            with_in(std::integral_constant<int, kOutF32>{});
+        else
+            with_in(std::integral_constant<int, kOutNone>{});
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,

@@ -49,6 +49,9 @@ hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8
                            hipStream_t st);
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
                          float* scales_out, void* out, int out_kind, hipStream_t st);
+hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
+                                  size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
+                                  float* scales_out, void* out, int out_kind, hipStream_t st);
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
                             size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st);
 hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,

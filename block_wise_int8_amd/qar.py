@@ -29,6 +29,7 @@ _vp, _sz, _u32, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes
 _SIGNATURES = {
     "qar_quantize_blocks": [_vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_reduce_quantized": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_quantize_reduce": [_vp, _int, _u32, _vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
     "qar_reduce_quantized_pipelined": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _u32, _vp, _u32, _vp],
     "qar_ring_step": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
@@ -162,6 +163,29 @@ def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], 
                                       _dev(codes_out, "codes_out").data_ptr(),
                                       _dev(scales_out, "scales_out").data_ptr(), optr, odt,
                                       _stream(stream)), "qar_reduce_quantized")
+    return codes_out, scales_out
+
+
+def qar_quantize_reduce(x_own: torch.Tensor, own: int, codes: list[torch.Tensor], scales: list[torch.Tensor],
+                        block: int, codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, stream=None):
+    """Quantize x_own into codes[own]/scales[own] and reduce all ranks in the
+    same pass -> (codes_out, scales_out); ``out`` gets the dequantized result."""
+    if len(codes) != len(scales) or not codes:
+        raise ValueError("need one scales tensor per codes tensor, at least one rank")
+    _dev(x_own, "x_own")
+    n = x_own.numel()
+    dev = x_own.device
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=torch.int8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
+    optr, odt = _out_args(out)
+    cp, sp = _ptrs(codes), _ptrs(scales)
+    _check(lib().qar_quantize_reduce(x_own.data_ptr(), _dtype_code(x_own.dtype), own, ctypes.cast(cp, _vp),
+                                     ctypes.cast(sp, _vp), len(codes), n, block,
+                                     _dev(codes_out, "codes_out").data_ptr(), _dev(scales_out, "scales_out").data_ptr(),
+                                     optr, odt, _stream(stream)), "qar_quantize_reduce")
     return codes_out, scales_out
 
 

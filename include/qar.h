@@ -116,6 +116,28 @@ qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* 
                                 void* out, qar_dtype out_dtype, void* stream);
 
 /*
+ * This rank's quantize fused into the reduce: the one-shot reduce in which
+ * rank `own` contributes its unquantized buffer x_own.  x_own is quantized in
+ * the same pass ("technical framework" step 2), its codes and scales are
+ * written to codes[own] / scales[own] (what the peers receive), and those
+ * same values enter the rank-order sum ("technical framework" step 3).
+ * Results (codes[own], scales[own], codes_out, scales_out, out) are
+ * bit-identical to qar_quantize_blocks(x_own -> codes[own], scales[own])
+ * followed by qar_reduce_quantized; x_own is read once and codes[own] is
+ * never read back.
+ *   x_own        [in]  n elements of dtype (bf16 or fp32).
+ *   own          0 .. nranks-1.
+ *   codes, scales HOST arrays of nranks DEVICE pointers; entry own is an
+ *                output, the others are inputs (as in qar_reduce_quantized).
+ *   codes_out, scales_out, out, out_dtype  as in qar_reduce_quantized, but
+ *                they may not be rank own's buffers.
+ */
+qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
+                               float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                               int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                               void* stream);
+
+/*
  * The same reduce, cut into `nchunks` block-aligned chunks that are
  * enqueued round-robin on `streams[0 .. nstreams-1]`, so that one chunk's
  * loads overlap another chunk's arithmetic (the pages' pipelining of

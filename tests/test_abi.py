@@ -67,6 +67,28 @@ def test_reduce_validation(L):
     assert r(codes, scales, 2, 256, 256, 0x50000, 0x60000, 0x70000, 9, None) == qar.QAR_ERR_UNSUPPORTED
 
 
+def test_quantize_reduce_validation(L):
+    r = L.qar_quantize_reduce
+    X = 0x80000
+    codes, scales = _arr(A, B_), _arr(C, D)
+    ok = (codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, None)
+    assert r(None, 0, 0, None, None, 2, 0, 256, None, None, None, 0, None) == qar.QAR_OK
+    assert r(None, 0, 0, *ok) == qar.QAR_ERR_INVALID_ARG
+    assert r(X, 7, 0, *ok) == qar.QAR_ERR_UNSUPPORTED                        # input dtype
+    assert r(X, 0, 2, *ok) == qar.QAR_ERR_INVALID_ARG                        # own >= nranks
+    assert r(X + 2, 0, 0, *ok) == qar.QAR_ERR_MISALIGNED
+    assert r(X, 0, 0, codes, scales, 2, 256, 96, 0x50000, 0x60000, None, 0, None) == qar.QAR_ERR_UNSUPPORTED
+    # rank own's codes (an output) may not be the result's codes, even in place
+    assert r(X, 0, 1, codes, scales, 2, 256, 256, B_, D, None, 0, None) == qar.QAR_ERR_INVALID_ARG
+    # the input may not overlap rank own's codes or the result
+    assert r(A + 128, 0, 0, *ok) == qar.QAR_ERR_INVALID_ARG
+    assert r(0x50000, 0, 0, *ok) == qar.QAR_ERR_INVALID_ARG
+    assert r(X, 0, 0, codes, scales, 2, 256, 256, 0x50000, 0x60000, X + 64, 0, None) == qar.QAR_ERR_INVALID_ARG
+    # rank own's codes overlapping another rank's scales
+    assert r(X, 0, 0, _arr(A, B_), _arr(A + 64, D), 2, 256, 256, 0x50000, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_INVALID_ARG
+
+
 def test_pipelined_validation(L):
     p = L.qar_reduce_quantized_pipelined
     codes, scales = _arr(A, B_), _arr(C, D)

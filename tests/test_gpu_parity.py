@@ -189,6 +189,38 @@ def test_reduce_in_place(oracle_lib):
     assert_same_f32(to_host(ds[2]), ws, "scales")
 
 
+@pytest.mark.parametrize("block", qar.BLOCK_SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nranks,own", [(1, 0), (3, 1), (8, 0), (8, 7), (9, 8), (32, 13)])
+def test_quantize_reduce_parity(oracle_lib, nranks, own, dtype, block):
+    """The fused call: rank own quantized from its raw data in the same pass
+    as the reduce.  Its codes and scales, and the result, equal the oracle's
+    quantize followed by its reduce."""
+    n = ragged_n(block, tiles=2)
+    make = mixed_bf16 if dtype == "bf16" else mixed_f32
+    xs = [make(300 * nranks + r, n, block, SUM_OUTLIER) for r in range(nranks)]
+    codes, scales = _rank_codes(oracle_lib, xs, block)
+    say(f"quantize_reduce N={nranks} own={own} {dtype} B={block} n={n}")
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    dc[own].fill_(0x55)                      # written by the call
+    ds[own].fill_(-1.0)
+    out = torch.empty(n, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda:0")
+    oc, os_ = qar.qar_quantize_reduce(to_dev(xs[own]), own, dc, ds, block, out=out)
+    oc2, os2 = qar.qar_quantize_reduce(to_dev(xs[own]), own, dc, ds, block)
+    torch.cuda.synchronize()
+    assert_same_codes(to_host(dc[own]), codes[own], "own codes")
+    assert_same_f32(to_host(ds[own]), scales[own], "own scales")
+    wc, ws = oracle_lib.reduce(codes, scales, block)
+    for c, s in ((oc, os_), (oc2, os2)):
+        assert_same_codes(to_host(c), wc, "codes")
+        assert_same_f32(to_host(s), ws, "scales")
+    want = oracle_lib.dequantize(wc, ws, block, dtype)
+    if dtype == "bf16":
+        assert_same_bits16(to_host(out), want, "fused out")
+    else:
+        assert_same_f32(to_host(out), want, "fused out")
+
+
 @pytest.mark.parametrize("nstreams", [1, 4])
 @pytest.mark.parametrize("nchunks", [1, 3, 8, 16, 64])
 def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):

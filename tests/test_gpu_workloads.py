@@ -1,7 +1,8 @@
 """Every workload at its full size, through the C ABI, against the CPU
 oracle on every element: quantize each rank, then the one-shot reduce with
 its fused dequantized output (the small-block fp32 workload through the
-4-stream pipelined call, as it is specified), or the N-1 ring steps; plus
+4-stream pipelined call, as it is specified; the bf16 workloads also as
+the one-kernel quantize-and-reduce), or the N-1 ring steps; plus
 the error bounds against the exact fp64 sum on sampled blocks.
 
 Workloads (seeded, block_wise_int8_amd/synth.py):
@@ -85,6 +86,20 @@ def test_one_shot_workload(oracle_lib, key):
     else:
         assert_same_f32(got_out, want_out, f"{key} fused dequantize")
     say(f"{key}: reduce + fused dequantize bit-exact")
+    if key != "smallblock":
+        # the step as one kernel: rank 0 quantized from its raw data in the
+        # reduce's pass, into fresh buffers
+        own_c = torch.full_like(dc[0], 0x55)
+        own_s = torch.full_like(ds[0], -1.0)
+        out2 = torch.empty_like(out)
+        fc, fs = qar.qar_quantize_reduce(to_dev(host[0]), 0, [own_c] + dc[1:], [own_s] + ds[1:], w.block, out=out2)
+        torch.cuda.synchronize()
+        assert_same_codes(to_host(own_c), oc[0], f"{key} fused own codes")
+        assert_same_f32(to_host(own_s), os_[0], f"{key} fused own scales")
+        assert_same_codes(to_host(fc), wc, f"{key} fused step codes")
+        assert_same_f32(to_host(fs), ws, f"{key} fused step scales")
+        assert_same_bits16(to_host(out2), want_out, f"{key} fused step out")
+        say(f"{key}: quantize + reduce in one kernel bit-exact")
 
     # error against the exact sum on sampled blocks
     picks, idx = _sample_blocks(w)
