@@ -642,31 +642,67 @@ def ring_bench(qar, torch, np, synth, dev):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def _cpu_threads() -> int:
+    try:
+        t = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        t = os.cpu_count() or 1
+    return max(1, min(t, 16))
+
+
 def cpu_baseline(args, np, w, host, set0, torch):
-    """The CPU oracle (plain scalar C, one thread) running the same step on
-    the same inputs: quantize rank 0, reduce the N quantized ranks, dequantize
-    the result.  Also checks the GPU step's output against it."""
+    """The CPU oracle (plain scalar C) running the same step on the same
+    inputs: quantize rank 0, reduce the N quantized ranks, dequantize the
+    result.  Timed on one host thread over the whole buffer, then on T
+    threads, each running the same oracle calls on its own block-aligned
+    range (ctypes releases the GIL during the calls).  Also checks the GPU
+    step's output against the oracle's."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     o = oracle.load()
     B = w.block
+    kind = "bf16" if w.dtype == "bf16" else "f32"
     qs = [o.quantize(x, B) for x in host]          # peers' contributions (untimed)
     codes = [q[0] for q in qs]
     scales = [q[1] for q in qs]
+
+    def step(lo, hi):
+        c0, s0 = o.quantize(host[0][lo:hi], B)
+        oc, os_ = o.reduce([c0] + [c[lo:hi] for c in codes[1:]],
+                           [s0] + [s[lo // B:hi // B] for s in scales[1:]], B)
+        return c0, oc, o.dequantize(oc, os_, B, kind)
+
     reps = max(1, args.cpu_reps)
     t0 = time.perf_counter()
     for _ in range(reps):
-        c0, s0 = o.quantize(host[0], B)
-        oc, os_ = o.reduce([c0] + codes[1:], [s0] + scales[1:], B)
-        y = o.dequantize(oc, os_, B, "bf16" if w.dtype == "bf16" else "f32")
-    dt = (time.perf_counter() - t0) / reps
+        c0, oc, y = step(0, w.n)
+    dt1 = (time.perf_counter() - t0) / reps
+
+    T = _cpu_threads()
+    nb = w.n // B
+    cuts = [(nb * k // T) * B for k in range(T + 1)]
+    with ThreadPoolExecutor(T) as pool:
+        list(pool.map(lambda k: step(cuts[k], cuts[k + 1]), range(T)))           # warm the pool
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            parts = list(pool.map(lambda k: step(cuts[k], cuts[k + 1]), range(T)))
+        dtT = (time.perf_counter() - t0) / reps
+    same_split = all(np.array_equal(p[1], oc[cuts[k]:cuts[k + 1]]) for k, p in enumerate(parts))
+
     gpu_codes = set0["codes_out"].cpu().numpy()
     gpu_out = set0["out"].contiguous().view(torch.int16 if w.dtype == "bf16" else torch.int32).cpu().numpy()
     own_codes = set0["codes"][0].cpu().numpy()         # written by the step for the peers
     same = (bool(np.array_equal(gpu_codes, oc)) and bool(np.array_equal(gpu_out.view(y.dtype), y))
             and bool(np.array_equal(own_codes, c0)))
-    return {"value": round(w.nranks * w.n * 2 / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    payload = w.nranks * w.n * 2
+    return {"value": round(payload / dtT / 1e9, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
             "sample": f"the whole workload, {reps} repetitions of the step (quantize own buffer, reduce "
-                      f"{w.nranks} ranks, dequantize); {dt:.3f} s per step on one host thread",
+                      f"{w.nranks} ranks, dequantize) on {T} host threads, each on its own block range; "
+                      f"{dtT:.3f} s per step",
+            "single_thread": {"value": round(payload / dt1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "seconds_per_step": round(dt1, 4)},
+            "threads_agree_with_single_thread": bool(same_split),
             "gpu_output_matches_oracle": same}
 
 
