@@ -55,8 +55,18 @@ class Oracle:
         lib.oracle_reduce_unquantized.argtypes = [vp, ctypes.c_int, sz, sz, vp]
         lib.oracle_f32_to_bf16.argtypes = [vp, sz, vp]
         lib.oracle_f32_to_bf16.restype = None
+        lib.oracle_quantize_e4m3.argtypes = [vp, ctypes.c_int, sz, sz, vp, vp]
+        lib.oracle_dequantize_e4m3.argtypes = [vp, vp, sz, sz, ctypes.c_int, vp]
+        lib.oracle_reduce_e4m3.argtypes = [vp, vp, sz, sz, sz, vp, vp]
+        lib.oracle_ring_step_e4m3.argtypes = [vp, vp, vp, ctypes.c_int, sz, sz, vp, vp]
+        lib.oracle_e4m3_encode.argtypes = [vp, sz, vp]
+        lib.oracle_e4m3_encode.restype = None
+        lib.oracle_e4m3_decode.argtypes = [vp, sz, vp]
+        lib.oracle_e4m3_decode.restype = None
         for name in ("oracle_quantize", "oracle_dequantize_f32", "oracle_dequantize_bf16",
-                     "oracle_reduce", "oracle_ring_step", "oracle_reduce_unquantized"):
+                     "oracle_reduce", "oracle_ring_step", "oracle_reduce_unquantized",
+                     "oracle_quantize_e4m3", "oracle_dequantize_e4m3", "oracle_reduce_e4m3",
+                     "oracle_ring_step_e4m3"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
 
@@ -175,6 +185,81 @@ class Oracle:
         x = np.ascontiguousarray(x, np.float32).reshape(-1)
         out = np.empty(x.size, np.uint16)
         self.lib.oracle_f32_to_bf16(self._ptr(x), x.size, self._ptr(out))
+        return out
+
+    # -- FP8 E4M3 codes -------------------------------------------------
+    def quantize_e4m3(self, x: np.ndarray, block: int):
+        """x (bf16 uint16 patterns or float32) -> (E4M3 codes uint8[n], scales float32[nb])."""
+        x = np.ascontiguousarray(x).reshape(-1)
+        n = x.size
+        codes = np.empty(n, np.uint8)
+        scales = np.empty(self.nblocks(n, block), np.float32)
+        rc = self.lib.oracle_quantize_e4m3(self._ptr(x), self._dtype_of(x), n, block,
+                                           self._ptr(codes), self._ptr(scales))
+        self._check(rc, "quantize_e4m3")
+        return codes, scales
+
+    def dequantize_e4m3(self, codes: np.ndarray, scales: np.ndarray, block: int, out: str = "f32"):
+        codes = np.ascontiguousarray(codes, np.uint8).reshape(-1)
+        scales = np.ascontiguousarray(scales, np.float32).reshape(-1)
+        n = codes.size
+        if scales.size < self.nblocks(n, block):
+            raise ValueError("too few scales")
+        if out not in ("f32", "bf16"):
+            raise ValueError(out)
+        res = np.empty(n, np.float32 if out == "f32" else np.uint16)
+        rc = self.lib.oracle_dequantize_e4m3(self._ptr(codes), self._ptr(scales), n, block,
+                                             F32 if out == "f32" else BF16, self._ptr(res))
+        self._check(rc, "dequantize_e4m3")
+        return res
+
+    def reduce_e4m3(self, codes: list, scales: list, block: int):
+        nranks = len(codes)
+        if nranks == 0 or nranks != len(scales):
+            raise ValueError("need one scales array per codes array, at least one rank")
+        codes = [np.ascontiguousarray(c, np.uint8).reshape(-1) for c in codes]
+        scales = [np.ascontiguousarray(s, np.float32).reshape(-1) for s in scales]
+        n = codes[0].size
+        nb = self.nblocks(n, block)
+        for c, s in zip(codes, scales):
+            if c.size != n or s.size < nb:
+                raise ValueError("rank buffers differ in size")
+        cptr = (ctypes.c_void_p * nranks)(*[self._ptr(c) for c in codes])
+        sptr = (ctypes.c_void_p * nranks)(*[self._ptr(s) for s in scales])
+        out_c = np.empty(n, np.uint8)
+        out_s = np.empty(nb, np.float32)
+        rc = self.lib.oracle_reduce_e4m3(ctypes.cast(cptr, ctypes.c_void_p), ctypes.cast(sptr, ctypes.c_void_p),
+                                         nranks, n, block, self._ptr(out_c), self._ptr(out_s))
+        self._check(rc, "reduce_e4m3")
+        return out_c, out_s
+
+    def ring_step_e4m3(self, codes_in: np.ndarray, scales_in: np.ndarray, local: np.ndarray, block: int):
+        codes_in = np.ascontiguousarray(codes_in, np.uint8).reshape(-1)
+        scales_in = np.ascontiguousarray(scales_in, np.float32).reshape(-1)
+        local = np.ascontiguousarray(local).reshape(-1)
+        n = codes_in.size
+        if local.size != n or scales_in.size < self.nblocks(n, block):
+            raise ValueError("size mismatch")
+        out_c = np.empty(n, np.uint8)
+        out_s = np.empty(self.nblocks(n, block), np.float32)
+        rc = self.lib.oracle_ring_step_e4m3(self._ptr(codes_in), self._ptr(scales_in), self._ptr(local),
+                                            self._dtype_of(local), n, block, self._ptr(out_c), self._ptr(out_s))
+        self._check(rc, "ring_step_e4m3")
+        return out_c, out_s
+
+    def e4m3_encode(self, x: np.ndarray) -> np.ndarray:
+        """float32 values with |x| <= 448 -> nearest E4M3 codes (ties to even)."""
+        x = np.ascontiguousarray(x, np.float32).reshape(-1)
+        if np.any(np.abs(x) > 448.0) or not np.all(np.isfinite(x)):
+            raise ValueError("e4m3_encode takes finite values within [-448, 448]")
+        out = np.empty(x.size, np.uint8)
+        self.lib.oracle_e4m3_encode(self._ptr(x), x.size, self._ptr(out))
+        return out
+
+    def e4m3_decode(self, c: np.ndarray) -> np.ndarray:
+        c = np.ascontiguousarray(c, np.uint8).reshape(-1)
+        out = np.empty(c.size, np.float32)
+        self.lib.oracle_e4m3_decode(self._ptr(c), c.size, self._ptr(out))
         return out
 
 

@@ -96,3 +96,46 @@ def ring_bound_simple(step_scales, exact_sum: np.ndarray, block: int) -> np.ndar
     for s in step_scales:
         b += per_element(s, block, n) / 2.0
     return b + 1e-6 * np.abs(exact_sum)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 codes.  An E4M3 value has 3 mantissa bits: on [2^e, 2^(e+1)),
+# e >= -6, neighbours are 2^(e-3) apart, so rounding a quotient t moves it by
+# at most 2^-4 |t|; below 2^-6 the spacing is the subnormal step 2^-9, so at
+# most 2^-10.  With the quotient and product roundings (u each):
+#
+#   |x - fl32(e4m3(t) * s)| <= (2^-4 + 4u) |x| + (2^-10 + u) s      (1e)
+#
+# (u|y| <= 2u|x| + u s because |y| <= (1 + 2^-3)|x| + 2^-9 s).  The one-shot
+# and ring bounds are (3) and (4) above with (1e) in place of (1).
+
+E4M3_REL = 2.0 ** -4 + 4 * U
+E4M3_ABS = 2.0 ** -10 + U
+
+
+def requant_bound_e4m3(x_abs: np.ndarray, s_elem: np.ndarray) -> np.ndarray:
+    """(1e): bound on |x - dequantize(quantize(x))| for E4M3 codes."""
+    return E4M3_REL * x_abs + E4M3_ABS * s_elem + 2 * TINY
+
+
+def oneshot_bound_e4m3(xs, scales_in, ys, scale_out, block: int) -> np.ndarray:
+    n = np.asarray(xs[0]).size
+    nr = len(xs)
+    sum_abs_y = np.zeros(n)
+    bound = np.zeros(n)
+    for x, s, y in zip(xs, scales_in, ys):
+        bound += requant_bound_e4m3(np.abs(np.asarray(x, np.float64).reshape(-1)), per_element(s, block, n))
+        sum_abs_y += np.abs(np.asarray(y, np.float64).reshape(-1))
+    g = gamma(nr - 1)
+    bound += g * sum_abs_y + nr * TINY
+    bound += requant_bound_e4m3((1.0 + g) * sum_abs_y, per_element(scale_out, block, n))
+    return bound
+
+
+def ring_bound_e4m3(step_scales, step_values, block: int) -> np.ndarray:
+    n = np.asarray(step_values[0]).size
+    b = np.zeros(n)
+    for s, p in zip(step_scales, step_values):
+        pa = np.abs(np.asarray(p, np.float64).reshape(-1))
+        b += requant_bound_e4m3(pa, per_element(s, block, n)) + U * pa + TINY
+    return b

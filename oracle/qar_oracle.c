@@ -271,3 +271,212 @@ void oracle_f32_to_bf16(const float* in, size_t n, uint16_t* out)
     for (size_t i = 0; i < n; i++)
         out[i] = float_to_bf16_bits(in[i]);
 }
+
+/* ------------------------------------------------------------------------
+ * FP8 E4M3 codes: the same block-wise method with 8-bit floating-point codes
+ * instead of integers.  "TACO: Tensor-parallel Adaptive COmmunication
+ * compression" (page summary), section "Why FP8?": the E4M3 format's
+ * exponential spacing keeps precision for the many small values and range
+ * for the outliers; section "Dual-Scale quantization": a per-block scale
+ * brings the block into FP8's dynamic range, Q_max.  Only that single
+ * post-scale is taken here (no rotation, no pre-scale).
+ *
+ * E4M3 as defined by the OCP 8-bit floating point specification: sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m/8 * 2^-6; exponent field 15 with mantissa 7 is NaN and there
+ * is no infinity, so the largest finite value is 1.75 * 2^8 = 448 (Q_max).
+ *
+ * Readings:
+ *   scale  s   = fl32(absmax / 448)
+ *   code   c_i = 0x00                                        if s == 0
+ *              = E4M3 nearest to clamp(fl32(x_i / s), -448, 448), ties to
+ *                the even code; the sign is kept, so a negative quotient
+ *                that rounds to zero gives 0x80 (-0)
+ *   value  y_i = fl32(e4m3(c_i) * s)
+ *   reduce and ring: as for int8 codes, with this quantizer and value.
+ * ------------------------------------------------------------------------ */
+
+#define E4M3_MAX 448.0f
+
+/* The value of an E4M3 code, from the format's definition (NaN codes give
+ * NaN). */
+static float e4m3_value(uint8_t c)
+{
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    float mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexpf((float)m, -9);                 /* (m/8) * 2^-6 */
+    else
+        mag = ldexpf((float)(8 + m), e - 10);       /* (1 + m/8) * 2^(e-7) */
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* The E4M3 code nearest to t, |t| <= 448, ties to the code whose mantissa
+ * (lowest bit) is even.  The finite non-negative codes 0..126 are in
+ * increasing order of value, so a linear walk finds the neighbours below
+ * and above |t|; both distances are exact in binary64. */
+static uint8_t e4m3_nearest(float t)
+{
+    uint8_t sign = signbit(t) ? 0x80 : 0x00;
+    float a = fabsf(t);
+    unsigned c = 0;
+    while (c < 126 && e4m3_value((uint8_t)(c + 1)) <= a)
+        c++;
+    if (c < 126) {
+        double below = (double)a - (double)e4m3_value((uint8_t)c);
+        double above = (double)e4m3_value((uint8_t)(c + 1)) - (double)a;
+        if (above < below || (above == below && (c & 1u)))
+            c++;
+    }
+    return (uint8_t)(sign | c);
+}
+
+static void quantize_one_block_e4m3(const float* v, size_t len, uint8_t* q, float* scale)
+{
+    float absmax = 0.0f;
+    for (size_t i = 0; i < len; i++) {
+        float m = fabsf(v[i]);
+        if (m > absmax)
+            absmax = m;
+    }
+    float s = absmax / E4M3_MAX;
+    *scale = s;
+    for (size_t i = 0; i < len; i++) {
+        if (s == 0.0f) {
+            q[i] = 0x00;
+            continue;
+        }
+        float t = v[i] / s;
+        if (t > E4M3_MAX)
+            t = E4M3_MAX;
+        if (t < -E4M3_MAX)
+            t = -E4M3_MAX;
+        q[i] = e4m3_nearest(t);
+    }
+}
+
+static float dequant_value_e4m3(uint8_t c, float s) { return e4m3_value(c) * s; }
+
+/* x: n elements of dtype; codes: E4M3 bytes[n]; scales: fp32[ceil(n/block)]. */
+int oracle_quantize_e4m3(const void* x, int dtype, size_t n, size_t block,
+                         uint8_t* codes, float* scales)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!x || !codes || !scales)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(x, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* v = malloc(block * sizeof *v);
+    if (!v)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            v[i] = load_element(x, dtype, start + i);
+        quantize_one_block_e4m3(v, len, codes + start, scales + b);
+    }
+    free(v);
+    return ORACLE_OK;
+}
+
+/* out: fp32[n] (out_dtype ORACLE_F32) or bf16 patterns (ORACLE_BF16). */
+int oracle_dequantize_e4m3(const uint8_t* codes, const float* scales, size_t n,
+                           size_t block, int out_dtype, void* out)
+{
+    if (block == 0 || (out_dtype != ORACLE_BF16 && out_dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++) {
+        float y = dequant_value_e4m3(codes[i], scales[i / block]);
+        if (out_dtype == ORACLE_BF16)
+            ((uint16_t*)out)[i] = float_to_bf16_bits(y);
+        else
+            ((float*)out)[i] = y;
+    }
+    return ORACLE_OK;
+}
+
+/* One-shot N-way reduce of E4M3-coded ranks, rank order 0..N-1. */
+int oracle_reduce_e4m3(const uint8_t* const* codes, const float* const* scales,
+                       size_t nranks, size_t n, size_t block,
+                       uint8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || nranks == 0)
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value_e4m3(codes[0][start + i], scales[0][b]);
+        for (size_t r = 1; r < nranks; r++)
+            for (size_t i = 0; i < len; i++)
+                acc[i] = acc[i] + dequant_value_e4m3(codes[r][start + i], scales[r][b]);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
+        quantize_one_block_e4m3(acc, len, codes_out + start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}
+
+/* One ring step with E4M3 codes: dequantize, add the local values, quantize. */
+int oracle_ring_step_e4m3(const uint8_t* codes_in, const float* scales_in,
+                          const void* local, int dtype, size_t n, size_t block,
+                          uint8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(local, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value_e4m3(codes_in[start + i], scales_in[b]) +
+                     load_element(local, dtype, start + i);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
+        quantize_one_block_e4m3(acc, len, codes_out + start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}
+
+/* The E4M3 encoding and decoding on their own, so that tests can pin them
+ * to a library conversion.  encode expects |in[i]| <= 448. */
+void oracle_e4m3_encode(const float* in, size_t n, uint8_t* out)
+{
+    for (size_t i = 0; i < n; i++)
+        out[i] = e4m3_nearest(in[i]);
+}
+
+void oracle_e4m3_decode(const uint8_t* in, size_t n, float* out)
+{
+    for (size_t i = 0; i < n; i++)
+        out[i] = e4m3_value(in[i]);
+}

@@ -144,3 +144,103 @@ def reduce(rank_codes: list[list[int]], rank_scales: list[list[Fraction]], block
 def ring_step(codes: list[int], scales: list[Fraction], local: list[Fraction], block: int):
     y = dequantize(codes, scales, block)
     return quantize([rn32(a + b) for a, b in zip(y, local)], block)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 codes ("TACO" page, sections "Why FP8?" and "Dual-Scale
+# quantization"; format from the OCP 8-bit floating point specification).
+# Every finite E4M3 value is listed from the format's fields; the nearest one
+# is found by scanning the whole list, ties to the code with an even
+# mantissa.
+
+E4M3_QMAX = Fraction(448)
+
+
+def e4m3_exact(code: int) -> Fraction | None:
+    """Exact value of an E4M3 byte; None for the two NaN codes."""
+    code = int(code)
+    sign = -1 if code & 0x80 else 1
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    if e == 0:
+        return sign * Fraction(m, 8) * _TWO ** -6
+    return sign * (1 + Fraction(m, 8)) * _TWO ** (e - 7)
+
+
+E4M3_FINITE = [(c, e4m3_exact(c)) for c in range(256) if e4m3_exact(c) is not None]
+
+
+def e4m3_nearest_code(t: Fraction, negative: bool) -> int:
+    """The E4M3 code nearest to t (|t| <= 448); ties to the even mantissa.
+    A result of zero takes the sign of the quotient (`negative`), which t
+    alone cannot carry once it has rounded to 0."""
+    best = None
+    for c, v in E4M3_FINITE:
+        d = abs(t - v)
+        key = (d, c & 1)                              # smaller distance, then even mantissa
+        if best is None or key < best[0]:
+            best = (key, c)
+    c = best[1]
+    if e4m3_exact(c) == 0:
+        c = 0x80 if negative else 0x00
+    return c
+
+
+def quantize_block_e4m3(values: list[Fraction], signs: list[bool] | None = None):
+    """One block of exact values -> (E4M3 codes, scale).  signs[i] marks an
+    input that is a negative zero."""
+    absmax = max((abs(v) for v in values), default=Fraction(0))
+    s = rn32(absmax / E4M3_QMAX)
+    if s == 0:
+        return [0x00] * len(values), s
+    out = []
+    for i, v in enumerate(values):
+        t = rn32(v / s)
+        t = max(-E4M3_QMAX, min(E4M3_QMAX, t))
+        out.append(e4m3_nearest_code(t, v < 0 or (v == 0 and bool(signs and signs[i]))))
+    return out, s
+
+
+def quantize_e4m3(values: list[Fraction], block: int, signs: list[bool] | None = None):
+    codes, scales = [], []
+    for start in range(0, len(values), block):
+        c, s = quantize_block_e4m3(values[start:start + block], signs[start:start + block] if signs else None)
+        codes += c
+        scales.append(s)
+    return codes, scales
+
+
+def dequantize_e4m3(codes: list[int], scales: list[Fraction], block: int) -> list[Fraction]:
+    return [rn32(e4m3_exact(c) * scales[i // block]) for i, c in enumerate(codes)]
+
+
+def _neg_zero_flags(codes: list[int], scales: list[Fraction], block: int) -> list[bool]:
+    """Which dequantized values are -0 in binary32: a -0 code times a
+    positive scale (a zero scale only comes with +0 codes)."""
+    return [c == 0x80 and scales[i // block] > 0 for i, c in enumerate(codes)]
+
+
+def reduce_e4m3(rank_codes: list[list[int]], rank_scales: list[list[Fraction]], block: int):
+    """Dequantize every rank, add in rank order (one rounding per add),
+    quantize the sum.  A binary32 sum is -0 only when both addends are -0."""
+    acc = dequantize_e4m3(rank_codes[0], rank_scales[0], block)
+    neg = _neg_zero_flags(rank_codes[0], rank_scales[0], block)
+    for c, s in zip(rank_codes[1:], rank_scales[1:]):
+        y = dequantize_e4m3(c, s, block)
+        ny = _neg_zero_flags(c, s, block)
+        new = [rn32(a + b) for a, b in zip(acc, y)]
+        neg = [n == 0 and a == 0 and b == 0 and na and nb
+               for n, a, b, na, nb in zip(new, acc, y, neg, ny)]
+        acc = new
+    return quantize_e4m3(acc, block, neg)
+
+
+def ring_step_e4m3(codes: list[int], scales: list[Fraction], local: list[Fraction],
+                   local_neg_zero: list[bool], block: int):
+    y = dequantize_e4m3(codes, scales, block)
+    ny = _neg_zero_flags(codes, scales, block)
+    acc = [rn32(a + b) for a, b in zip(y, local)]
+    neg = [v == 0 and a == 0 and b == 0 and na and nb
+           for v, a, b, na, nb in zip(acc, y, local, ny, local_neg_zero)]
+    return quantize_e4m3(acc, block, neg)
