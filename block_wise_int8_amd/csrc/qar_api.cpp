@@ -147,8 +147,8 @@ const char* qar_status_string(qar_status s) {
 
 const char* qar_last_error(void) { return g_last_error; }
 
-qar_status qar_quantize_blocks(const void* x, qar_dtype dtype, size_t n, uint32_t block, int8_t* codes,
-                               float* scales, void* stream) {
+static qar_status quantize_impl(const void* x, qar_dtype dtype, size_t n, uint32_t block, int8_t* codes,
+                                float* scales, void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
     qar_status st = check_common(n, block);
     if (st != QAR_OK) return st;
@@ -159,27 +159,52 @@ qar_status qar_quantize_blocks(const void* x, qar_dtype dtype, size_t n, uint32_
                 so = range(scales, n / block * 4);
     if (overlap(xi, co) || overlap(xi, so) || overlap(co, so)) return QAR_ERR_INVALID_ARG;
     const hipError_t e = qar::launch_quantize(x, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, n,
-                                              (int)block, codes, scales, (hipStream_t)stream);
-    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_quantize_blocks");
+                                              (int)block, codes, scales, (hipStream_t)stream, code);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, name);
 }
 
-qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
-                                size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* out,
-                                qar_dtype out_dtype, void* stream) {
+qar_status qar_quantize_blocks(const void* x, qar_dtype dtype, size_t n, uint32_t block, int8_t* codes,
+                               float* scales, void* stream) {
+    return quantize_impl(x, dtype, n, block, codes, scales, stream, qar::kCodeInt8, "qar_quantize_blocks");
+}
+
+qar_status qar_quantize_blocks_e4m3(const void* x, qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes,
+                                    float* scales, void* stream) {
+    return quantize_impl(x, dtype, n, block, (int8_t*)codes, scales, stream, qar::kCodeE4M3,
+                         "qar_quantize_blocks_e4m3");
+}
+
+static qar_status reduce_impl(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
+                              uint32_t block, int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                              void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
     qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
     if (st != QAR_OK) return st;
     qar::RankPtrs rp;
     fill_ranks(rp, codes, scales, nranks, 0, 0);
     const hipError_t e = qar::launch_reduce(rp, (int)nranks, n, (int)block, codes_out, scales_out, out,
-                                            out_kind(out, out_dtype), (hipStream_t)stream);
-    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized");
+                                            out_kind(out, out_dtype), (hipStream_t)stream, code);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, name);
 }
 
-qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
-                               float* const* scales, uint32_t nranks, size_t n, uint32_t block,
-                               int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
-                               void* stream) {
+qar_status qar_reduce_quantized(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* out,
+                                qar_dtype out_dtype, void* stream) {
+    return reduce_impl(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype, stream,
+                       qar::kCodeInt8, "qar_reduce_quantized");
+}
+
+qar_status qar_reduce_quantized_e4m3(const uint8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t n, uint32_t block, uint8_t* codes_out, float* scales_out, void* out,
+                                     qar_dtype out_dtype, void* stream) {
+    return reduce_impl((const int8_t* const*)codes, scales, nranks, n, block, (int8_t*)codes_out, scales_out, out,
+                       out_dtype, stream, qar::kCodeE4M3, "qar_reduce_quantized_e4m3");
+}
+
+static qar_status quantize_reduce_impl(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
+                                       float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                                       int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                                       void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
     if (!x_own || !codes || !scales) return QAR_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
@@ -210,8 +235,25 @@ qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own,
     fill_ranks(rp, (const int8_t* const*)codes, (const float* const*)scales, nranks, 0, 0);
     const hipError_t e = qar::launch_quantize_reduce(
         x_own, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, (int)own, rp, (int)nranks, n, (int)block,
-        codes[own], scales[own], codes_out, scales_out, out, out_kind(out, out_dtype), (hipStream_t)stream);
-    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_quantize_reduce");
+        codes[own], scales[own], codes_out, scales_out, out, out_kind(out, out_dtype), (hipStream_t)stream, code);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, name);
+}
+
+qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
+                               float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                               int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                               void* stream) {
+    return quantize_reduce_impl(x_own, dtype, own, codes, scales, nranks, n, block, codes_out, scales_out, out,
+                                out_dtype, stream, qar::kCodeInt8, "qar_quantize_reduce");
+}
+
+qar_status qar_quantize_reduce_e4m3(const void* x_own, qar_dtype dtype, uint32_t own, uint8_t* const* codes,
+                                    float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                                    uint8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                                    void* stream) {
+    return quantize_reduce_impl(x_own, dtype, own, (int8_t* const*)codes, scales, nranks, n, block,
+                                (int8_t*)codes_out, scales_out, out, out_dtype, stream, qar::kCodeE4M3,
+                                "qar_quantize_reduce_e4m3");
 }
 
 qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
@@ -258,8 +300,9 @@ qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const floa
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_pipelined");
 }
 
-qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, qar_dtype dtype,
-                         size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* stream) {
+static qar_status ring_step_impl(const int8_t* codes_in, const float* scales_in, const void* local,
+                                 qar_dtype dtype, size_t n, uint32_t block, int8_t* codes_out, float* scales_out,
+                                 void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
     qar_status st = check_common(n, block);
     if (st != QAR_OK) return st;
@@ -277,12 +320,25 @@ qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in, const v
     if ((co.lo == ci.lo) != (so.lo == si.lo)) return QAR_ERR_INVALID_ARG;
     const hipError_t e =
         qar::launch_ring_step(codes_in, scales_in, local, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, n,
-                              (int)block, codes_out, scales_out, (hipStream_t)stream);
-    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_ring_step");
+                              (int)block, codes_out, scales_out, (hipStream_t)stream, code);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, name);
 }
 
-qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
-                          qar_dtype out_dtype, void* stream) {
+qar_status qar_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, qar_dtype dtype,
+                         size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* stream) {
+    return ring_step_impl(codes_in, scales_in, local, dtype, n, block, codes_out, scales_out, stream,
+                          qar::kCodeInt8, "qar_ring_step");
+}
+
+qar_status qar_ring_step_e4m3(const uint8_t* codes_in, const float* scales_in, const void* local,
+                              qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes_out, float* scales_out,
+                              void* stream) {
+    return ring_step_impl((const int8_t*)codes_in, scales_in, local, dtype, n, block, (int8_t*)codes_out,
+                          scales_out, stream, qar::kCodeE4M3, "qar_ring_step_e4m3");
+}
+
+static qar_status dequantize_impl(const int8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                                  qar_dtype out_dtype, void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
     qar_status st = check_common(n, block);
     if (st != QAR_OK) return st;
@@ -293,8 +349,19 @@ qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, ui
                 oo = range(out, n * dtype_bytes(out_dtype));
     if (overlap(oo, ci) || overlap(oo, si)) return QAR_ERR_INVALID_ARG;
     const hipError_t e = qar::launch_dequantize(codes, scales, n, (int)block, out, out_kind(out, out_dtype),
-                                                (hipStream_t)stream);
-    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_dequantize");
+                                                (hipStream_t)stream, code);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, name);
+}
+
+qar_status qar_dequantize(const int8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                          qar_dtype out_dtype, void* stream) {
+    return dequantize_impl(codes, scales, n, block, out, out_dtype, stream, qar::kCodeInt8, "qar_dequantize");
+}
+
+qar_status qar_dequantize_e4m3(const uint8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                               qar_dtype out_dtype, void* stream) {
+    return dequantize_impl((const int8_t*)codes, scales, n, block, out, out_dtype, stream, qar::kCodeE4M3,
+                           "qar_dequantize_e4m3");
 }
 
 qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t n, qar_dtype dtype, void* out,

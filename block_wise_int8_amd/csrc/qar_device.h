@@ -181,6 +181,88 @@ __device__ __forceinline__ void dequantize16(uint4 q, float s, float (&y)[kLaneE
 }
 
 // ---------------------------------------------------------------------------
+// code formats.  Both are one byte per element, so every kernel's layout and
+// traffic is the same; the format decides Q_max (the value a block's absmax
+// maps to), how a quotient becomes a byte and what a byte is worth.
+
+// EQuARX's integers: q = clamp(rne(x/s), -127, 127), s = absmax / 127.
+struct Int8Codes {
+    static constexpr float kQmax = 127.0f;
+    static __device__ __forceinline__ float value(uint32_t w, int k) { return code_f32(w, k); }
+    static __device__ __forceinline__ uint4 quantize(const float (&v)[kLaneElems], float s) {
+        return quantize16(v, s);
+    }
+    static __device__ __forceinline__ void dequantize(uint4 q, float s, float (&y)[kLaneElems]) {
+        dequantize16(q, s, y);
+    }
+};
+
+// FP8 E4M3 in the OCP format (bias 7, 3 mantissa bits, no infinity, largest
+// finite 448), the format the TACO page argues for: s = absmax / 448 and the
+// code is the E4M3 value nearest to fl32(x / s) clamped to [-448, 448], ties
+// to even, sign kept.  gfx950's v_cvt_pk_fp8_f32 rounds to nearest even into
+// this format and v_cvt_f32_fp8 widens exactly.
+//
+// The quotient is the same exact FMA-corrected one as for int8, with a
+// higher threshold: quotients down to 2^-10 decide a code here (smaller
+// ones give +-0 with the sign of x), and for a quotient y >= 2^-11 the
+// remainder x - y*s is a multiple of 2^(-11-23) * 2^(-90-23) >= 2^-149, so
+// exact, when s >= 2^-90.  The FMA correction keeps a nonzero quotient's
+// sign; only x = -0 needs its sign restored.
+struct E4M3Codes {
+    static constexpr float kQmax = 448.0f;
+    static constexpr float kFastMinScale = 0x1p-90f;
+    static __device__ __forceinline__ float value(uint32_t w, int k) {
+        switch (k) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+        }
+    }
+    static __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+        a = __builtin_amdgcn_fmed3f(a, -kQmax, kQmax);
+        b = __builtin_amdgcn_fmed3f(b, -kQmax, kQmax);
+        c = __builtin_amdgcn_fmed3f(c, -kQmax, kQmax);
+        d = __builtin_amdgcn_fmed3f(d, -kQmax, kQmax);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+        return (uint32_t)w;
+    }
+    static __device__ __forceinline__ uint4 quantize(const float (&v)[kLaneElems], float s) {
+        float t[kLaneElems];
+        if (s >= kFastMinScale) {
+            const float r = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) {
+                float y = v[i] * r;
+                const float e = __builtin_fmaf(-y, s, v[i]);
+                // x = -0 gives e = +0 and +0 + -0 = +0: put the sign back
+                t[i] = __builtin_copysignf(__builtin_fmaf(e, r, y), v[i]);
+            }
+        } else if (s != 0.0f) {
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) t[i] = v[i] / s;
+        } else {
+            return make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint4 q;
+        q.x = pack4(t[0], t[1], t[2], t[3]);
+        q.y = pack4(t[4], t[5], t[6], t[7]);
+        q.z = pack4(t[8], t[9], t[10], t[11]);
+        q.w = pack4(t[12], t[13], t[14], t[15]);
+        return q;
+    }
+    static __device__ __forceinline__ void dequantize(uint4 q, float s, float (&y)[kLaneElems]) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[4 * j + k] = value(w[j], k) * s;
+    }
+};
+
+// ---------------------------------------------------------------------------
 // lane loads and stores of element data
 
 // A lane's 16 elements as loaded (32 bytes of bf16 or 64 of fp32), so a

@@ -83,7 +83,7 @@ __device__ __forceinline__ float masked_absmax(const float (&v)[kLaneElems], boo
 // ---------------------------------------------------------------------------
 // quantize: x (bf16 or fp32) -> codes, scales
 
-template <int B, typename In, typename Lanes>
+template <int B, typename In, typename Lanes, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x, Lanes lanes,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
         const size_t ld = a.valid ? a.e0 : 0;
         float v[kLaneElems];
         load16(x + ld, v);
-        const float s = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / 127.0f;
-        const uint4 q = quantize16(v, s);
+        const float s = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / C::kQmax;
+        const uint4 q = C::quantize(v, s);
         if (a.valid) {
             store_b128(codes + a.e0, q);
             if (a.leads) scales[a.blk] = s;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
 // fp32), so the codes and scales of the wave are staged in LDS and each lane
 // reads back the 8 (bf16) or 4 (fp32) codes that belong to its store slots.
 // Only lanes of one wavefront exchange data, so a wave barrier suffices.
-template <int B, int OUT>
+template <int B, int OUT, typename C = Int8Codes>
 __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_t e0, size_t n, void* out,
                                                        uint4* lds_codes, float* lds_scales) {
     constexpr int kLanesPerBlock = B / kLaneElems;
@@ -130,10 +130,10 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
             const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
             const float s = lds_scales[e / B];
             uint4 o;
-            o.x = pack_bf16x2(code_f32(c.x, 0) * s, code_f32(c.x, 1) * s);
-            o.y = pack_bf16x2(code_f32(c.x, 2) * s, code_f32(c.x, 3) * s);
-            o.z = pack_bf16x2(code_f32(c.y, 0) * s, code_f32(c.y, 1) * s);
-            o.w = pack_bf16x2(code_f32(c.y, 2) * s, code_f32(c.y, 3) * s);
+            o.x = pack_bf16x2(C::value(c.x, 0) * s, C::value(c.x, 1) * s);
+            o.y = pack_bf16x2(C::value(c.x, 2) * s, C::value(c.x, 3) * s);
+            o.z = pack_bf16x2(C::value(c.y, 0) * s, C::value(c.y, 1) * s);
+            o.w = pack_bf16x2(C::value(c.y, 2) * s, C::value(c.y, 3) * s);
             if (wave0 + e < n) store_b128(static_cast<uint16_t*>(out) + wave0 + e, o);
         }
     } else {
@@ -143,10 +143,10 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
             const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
             const float s = lds_scales[e / B];
             uint4 o;
-            o.x = __builtin_bit_cast(uint32_t, code_f32(c, 0) * s);
-            o.y = __builtin_bit_cast(uint32_t, code_f32(c, 1) * s);
-            o.z = __builtin_bit_cast(uint32_t, code_f32(c, 2) * s);
-            o.w = __builtin_bit_cast(uint32_t, code_f32(c, 3) * s);
+            o.x = __builtin_bit_cast(uint32_t, C::value(c, 0) * s);
+            o.y = __builtin_bit_cast(uint32_t, C::value(c, 1) * s);
+            o.z = __builtin_bit_cast(uint32_t, C::value(c, 2) * s);
+            o.w = __builtin_bit_cast(uint32_t, C::value(c, 3) * s);
             if (wave0 + e < n) store_b128(static_cast<float*>(out) + wave0 + e, o);
         }
     }
@@ -158,7 +158,7 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
 // `own` is quantized from x_own in the same pass: its codes and scale are
 // written for the peers and the same register values enter the sum, so the
 // result equals a quantize followed by the plain reduce.
-template <int B, int OUT, typename Lanes, typename OwnIn>
+template <int B, int OUT, typename Lanes, typename OwnIn, typename C>
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                              const OwnIn* __restrict__ x_own, int own,
@@ -194,8 +194,8 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
                 if (g == 0) {
                     float v[kLaneElems];
                     unpack16(xr, v);
-                    s_own = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / 127.0f;
-                    q_own = quantize16(v, s_own);
+                    s_own = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / C::kQmax;
+                    q_own = C::quantize(v, s_own);
                     if (a.valid) {
                         store_b128(own_codes + a.e0, q_own);
                         if (a.leads) own_scales[a.blk] = s_own;
@@ -213,7 +213,7 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
             for (int j = 0; j < G; ++j) {
                 if (g + j < nranks) {
                     float y[kLaneElems];
-                    dequantize16(q[j], s[j], y);
+                    C::dequantize(q[j], s[j], y);
                     if (g + j == 0) {
 #pragma unroll
                         for (int i = 0; i < kLaneElems; ++i) acc[i] = y[i];
@@ -224,16 +224,22 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
                 }
             }
         }
-        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / 127.0f;
+        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / C::kQmax;
         uint32_t w[kLaneElems];
-        const uint4 qo = quantize16(acc, so, w);
+        uint4 qo;
+        if constexpr (OUT != kOutNone && !kStaged) {
+            static_assert(std::is_same<C, Int8Codes>::value, "row-bounded output is int8 only");
+            qo = quantize16(acc, so, w);
+        } else {
+            qo = C::quantize(acc, so);
+        }
         if (a.valid) {
             store_b128(codes_out + a.e0, qo);
             if (a.leads) scales_out[a.blk] = so;
         }
         if constexpr (kStaged) {
             const int wave = threadIdx.x / 64;
-            store_dequantized_tile<B, OUT>(qo, so, a.e0, lanes.n, out, lds_codes + wave * 64,
+            store_dequantized_tile<B, OUT, C>(qo, so, a.e0, lanes.n, out, lds_codes + wave * 64,
                                            lds_scales + wave * (64 * kLaneElems / B));
         } else if constexpr (OUT != kOutNone) {
             // row-bounded blocks: a wave's elements are not one contiguous
@@ -250,28 +256,28 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
     }
 }
 
-template <int B, int OUT, typename Lanes>
+template <int B, int OUT, typename Lanes, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
                                                      int8_t* codes_out, float* scales_out,
                                                      void* __restrict__ out, uint32_t ntiles) {
-    reduce_tiles<B, OUT, Lanes, void>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr, -1,
-                                      nullptr, nullptr);
+    reduce_tiles<B, OUT, Lanes, void, C>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr, -1,
+                                         nullptr, nullptr);
 }
 
-template <int B, int OUT, typename In>
+template <int B, int OUT, typename In, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restrict__ x_own, int own,
                                                               int8_t* own_codes, float* own_scales,
                                                               RankPtrs rp, int nranks, FlatLanes<B> lanes,
                                                               int8_t* codes_out, float* scales_out,
                                                               void* __restrict__ out, uint32_t ntiles) {
-    reduce_tiles<B, OUT, FlatLanes<B>, In>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own, own,
-                                           own_codes, own_scales);
+    reduce_tiles<B, OUT, FlatLanes<B>, In, C>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own, own,
+                                              own_codes, own_scales);
 }
 
 // ---------------------------------------------------------------------------
 // ring step: dequantize incoming + add local (bf16/fp32) + requantize
 
-template <int B, typename In, typename Lanes>
+template <int B, typename In, typename Lanes, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, const float* scales_in,
                                                         const In* __restrict__ local, Lanes lanes,
                                                         int8_t* codes_out, float* scales_out,
@@ -286,12 +292,12 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
             const float s = scales_in[blk];
             float x[kLaneElems];
             load16(local + ld, x);
-            dequantize16(q, s, acc);
+            C::dequantize(q, s, acc);
 #pragma unroll
             for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + x[i];
         }
-        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / 127.0f;
-        const uint4 qo = quantize16(acc, so);
+        const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / C::kQmax;
+        const uint4 qo = C::quantize(acc, so);
         if (a.valid) {
             store_b128(codes_out + a.e0, qo);
             if (a.leads) scales_out[a.blk] = so;
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
 // 4L + 256j (fp32, j = 0..3) of the wave's 1024-element tile and reads the
 // 8 or 4 codes of each slot directly (8 or 4 bytes, 512 or 256 bytes
 // contiguous per load instruction).
-template <int B, typename Out>
+template <int B, typename Out, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restrict__ codes,
                                                          const float* __restrict__ scales, size_t n,
                                                          Out* __restrict__ out, uint32_t ntiles) {
@@ -324,16 +330,16 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
             uint4 o;
             if constexpr (kSlot == 8) {
                 const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
-                o.x = pack_bf16x2(code_f32(c.x, 0) * s, code_f32(c.x, 1) * s);
-                o.y = pack_bf16x2(code_f32(c.x, 2) * s, code_f32(c.x, 3) * s);
-                o.z = pack_bf16x2(code_f32(c.y, 0) * s, code_f32(c.y, 1) * s);
-                o.w = pack_bf16x2(code_f32(c.y, 2) * s, code_f32(c.y, 3) * s);
+                o.x = pack_bf16x2(C::value(c.x, 0) * s, C::value(c.x, 1) * s);
+                o.y = pack_bf16x2(C::value(c.x, 2) * s, C::value(c.x, 3) * s);
+                o.z = pack_bf16x2(C::value(c.y, 0) * s, C::value(c.y, 1) * s);
+                o.w = pack_bf16x2(C::value(c.y, 2) * s, C::value(c.y, 3) * s);
             } else {
                 const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
-                o.x = __builtin_bit_cast(uint32_t, code_f32(c, 0) * s);
-                o.y = __builtin_bit_cast(uint32_t, code_f32(c, 1) * s);
-                o.z = __builtin_bit_cast(uint32_t, code_f32(c, 2) * s);
-                o.w = __builtin_bit_cast(uint32_t, code_f32(c, 3) * s);
+                o.x = __builtin_bit_cast(uint32_t, C::value(c, 0) * s);
+                o.y = __builtin_bit_cast(uint32_t, C::value(c, 1) * s);
+                o.z = __builtin_bit_cast(uint32_t, C::value(c, 2) * s);
+                o.w = __builtin_bit_cast(uint32_t, C::value(c, 3) * s);
             }
             store_b128(out + e, o);
         }
@@ -656,56 +662,63 @@ hipError_t dispatch_block(int block, F&& f) {
     }
 }
 
-template <int B, typename Lanes>
+template <int B, typename Lanes, typename C = Int8Codes>
 hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* codes, float* scales,
                       hipStream_t st) {
     if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_quantize<B, uint16_t, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((k_quantize<B, uint16_t, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st,
                            static_cast<const uint16_t*>(x), lanes, codes, scales, g.ntiles);
     else
-        hipLaunchKernelGGL((k_quantize<B, float, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((k_quantize<B, float, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st,
                            static_cast<const float*>(x), lanes, codes, scales, g.ntiles);
     return hipGetLastError();
 }
 
-template <int B, typename Lanes>
+template <int B, typename Lanes, typename C = Int8Codes>
 hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t* codes_out, float* scales_out,
                     void* out, int out_kind, hipStream_t st) {
     if (out_kind == kOutBF16)
-        hipLaunchKernelGGL((k_reduce<B, kOutBF16, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+        hipLaunchKernelGGL((k_reduce<B, kOutBF16, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
                            lanes, codes_out, scales_out, out, g.ntiles);
     else if (out_kind == kOutF32)
-        hipLaunchKernelGGL((k_reduce<B, kOutF32, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+        hipLaunchKernelGGL((k_reduce<B, kOutF32, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
                            lanes, codes_out, scales_out, out, g.ntiles);
     else
-        hipLaunchKernelGGL((k_reduce<B, kOutNone, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
+        hipLaunchKernelGGL((k_reduce<B, kOutNone, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
                            lanes, codes_out, scales_out, out, g.ntiles);
     return hipGetLastError();
 }
 
-template <int B, typename Lanes>
+template <int B, typename Lanes, typename C = Int8Codes>
 hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind, Lanes lanes,
                   Grid g, int8_t* codes_out, float* scales_out, hipStream_t st) {
     if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_ring_step<B, uint16_t, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+        hipLaunchKernelGGL((k_ring_step<B, uint16_t, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
                            scales_in, static_cast<const uint16_t*>(local), lanes, codes_out, scales_out, g.ntiles);
     else
-        hipLaunchKernelGGL((k_ring_step<B, float, Lanes>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
+        hipLaunchKernelGGL((k_ring_step<B, float, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
                            scales_in, static_cast<const float*>(local), lanes, codes_out, scales_out, g.ntiles);
     return hipGetLastError();
 }
 
-template <int B>
+template <int B, typename C = Int8Codes>
 hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void* out, int out_kind,
                         hipStream_t st) {
     const Grid g = grid_for(n);
     if (out_kind == kOutBF16)
-        hipLaunchKernelGGL((k_dequantize<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, codes,
+        hipLaunchKernelGGL((k_dequantize<B, uint16_t, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes,
                            scales, n, static_cast<uint16_t*>(out), g.ntiles);
     else
-        hipLaunchKernelGGL((k_dequantize<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, codes, scales,
+        hipLaunchKernelGGL((k_dequantize<B, float, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes, scales,
                            n, static_cast<float*>(out), g.ntiles);
     return hipGetLastError();
+}
+
+// calls f(TypeTag<codes format>) for a code kind
+template <typename F>
+hipError_t dispatch_code(int code, F&& f) {
+    if (code == kCodeE4M3) return f(TypeTag<E4M3Codes>{});
+    return f(TypeTag<Int8Codes>{});
 }
 
 template <int B>
@@ -812,74 +825,85 @@ hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, 
 }
 
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
-                           hipStream_t st) {
+                           hipStream_t st, int code) {
     const Grid g = grid_for(n);
-    switch (block) {
-    case 64: return quantize_b<64>(x, in_kind, FlatLanes<64>{n}, g, codes, scales, st);
-    case 128: return quantize_b<128>(x, in_kind, FlatLanes<128>{n}, g, codes, scales, st);
-    default: return quantize_b<256>(x, in_kind, FlatLanes<256>{n}, g, codes, scales, st);
-    }
+    return dispatch_code(code, [&](auto ct) {
+        using C = typename decltype(ct)::type;
+        return dispatch_block(block, [&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            return quantize_b<B, FlatLanes<B>, C>(x, in_kind, FlatLanes<B>{n}, g, codes, scales, st);
+        });
+    });
 }
 
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st) {
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
     const Grid g = grid_for(n);
-    switch (block) {
-    case 64: return reduce_b<64>(rp, nranks, FlatLanes<64>{n}, g, codes_out, scales_out, out, out_kind, st);
-    case 128: return reduce_b<128>(rp, nranks, FlatLanes<128>{n}, g, codes_out, scales_out, out, out_kind, st);
-    default: return reduce_b<256>(rp, nranks, FlatLanes<256>{n}, g, codes_out, scales_out, out, out_kind, st);
-    }
+    return dispatch_code(code, [&](auto ct) {
+        using C = typename decltype(ct)::type;
+        return dispatch_block(block, [&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            return reduce_b<B, FlatLanes<B>, C>(rp, nranks, FlatLanes<B>{n}, g, codes_out, scales_out, out,
+                                                out_kind, st);
+        });
+    });
 }
 
 hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
-                                  float* scales_out, void* out, int out_kind, hipStream_t st) {
+                                  float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
     const Grid g = grid_for(n);
-    return dispatch_block(block, [&](auto bc) {
-        constexpr int B = decltype(bc)::value;
-        const FlatLanes<B> lanes{n};
-        auto go = [&](auto oc, auto in_tag) {
-            constexpr int OUT = decltype(oc)::value;
-            using In = typename decltype(in_tag)::type;
-            hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In>), dim3(g.blocks), dim3(kThreads), 0, st,
-                               static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
-                               codes_out, scales_out, out, g.ntiles);
-        };
-        auto with_in = [&](auto oc) {
-            if (in_kind == kInBF16)
-                go(oc, TypeTag<uint16_t>{});
+    return dispatch_code(code, [&](auto ct) {
+        using C = typename decltype(ct)::type;
+        return dispatch_block(block, [&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            const FlatLanes<B> lanes{n};
+            auto go = [&](auto oc, auto in_tag) {
+                constexpr int OUT = decltype(oc)::value;
+                using In = typename decltype(in_tag)::type;
+                hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C>), dim3(g.blocks), dim3(kThreads), 0, st,
+                                   static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
+                                   codes_out, scales_out, out, g.ntiles);
+            };
+            auto with_in = [&](auto oc) {
+                if (in_kind == kInBF16)
+                    go(oc, TypeTag<uint16_t>{});
+                else
+                    go(oc, TypeTag<float>{});
+            };
+            if (out_kind == kOutBF16)
+                with_in(std::integral_constant<int, kOutBF16>{});
+            else if (out_kind == kOutF32)
+                with_in(std::integral_constant<int, kOutF32>{});
             else
-                go(oc, TypeTag<float>{});
-        };
-        if (out_kind == kOutBF16)
-            with_in(std::integral_constant<int, kOutBF16>{});
-        else if (out_kind == kOutF32)
-            with_in(std::integral_constant<int, kOutF32>{});
-        else
-            with_in(std::integral_constant<int, kOutNone>{});
-        return hipGetLastError();
+                with_in(std::integral_constant<int, kOutNone>{});
+            return hipGetLastError();
+        });
     });
 }
 
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
-                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st) {
+                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st, int code) {
     const Grid g = grid_for(n);
-    switch (block) {
-    case 64: return ring_b<64>(codes_in, scales_in, local, in_kind, FlatLanes<64>{n}, g, codes_out, scales_out, st);
-    case 128:
-        return ring_b<128>(codes_in, scales_in, local, in_kind, FlatLanes<128>{n}, g, codes_out, scales_out, st);
-    default:
-        return ring_b<256>(codes_in, scales_in, local, in_kind, FlatLanes<256>{n}, g, codes_out, scales_out, st);
-    }
+    return dispatch_code(code, [&](auto ct) {
+        using C = typename decltype(ct)::type;
+        return dispatch_block(block, [&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            return ring_b<B, FlatLanes<B>, C>(codes_in, scales_in, local, in_kind, FlatLanes<B>{n}, g, codes_out,
+                                              scales_out, st);
+        });
+    });
 }
 
 hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,
-                             int out_kind, hipStream_t st) {
-    switch (block) {
-    case 64: return dequantize_b<64>(codes, scales, n, out, out_kind, st);
-    case 128: return dequantize_b<128>(codes, scales, n, out, out_kind, st);
-    default: return dequantize_b<256>(codes, scales, n, out, out_kind, st);
-    }
+                             int out_kind, hipStream_t st, int code) {
+    return dispatch_code(code, [&](auto ct) {
+        using C = typename decltype(ct)::type;
+        return dispatch_block(block, [&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            return dequantize_b<B, C>(codes, scales, n, out, out_kind, st);
+        });
+    });
 }
 
 } // namespace qar

@@ -13,6 +13,9 @@ constexpr int kMaxRanks = 32;
 
 enum : int { kInBF16 = 0, kInF32 = 1 };
 enum : int { kOutNone = -1, kOutBF16 = 0, kOutF32 = 1 };
+// code format of the flat calls: int8 integers or FP8 E4M3 bytes (the row-
+// bounded path is int8 only)
+enum : int { kCodeInt8 = 0, kCodeE4M3 = 1 };
 
 // Rank pointers travel in the kernel's argument segment (512 bytes).
 struct RankPtrs {
@@ -46,15 +49,17 @@ hipError_t launch_rows(const RowsCall& c, hipStream_t st);
 hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
                                      hipStream_t st);
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
-                           hipStream_t st);
+                           hipStream_t st, int code = kCodeInt8);
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st);
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code = kCodeInt8);
 hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
-                                  float* scales_out, void* out, int out_kind, hipStream_t st);
+                                  float* scales_out, void* out, int out_kind, hipStream_t st,
+                                  int code = kCodeInt8);
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
-                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st);
+                            size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st,
+                            int code = kCodeInt8);
 hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,
-                             int out_kind, hipStream_t st);
+                             int out_kind, hipStream_t st, int code = kCodeInt8);
 
 } // namespace qar

@@ -39,6 +39,11 @@ _SIGNATURES = {
     "qar_ring_step_rows": [_vp, _vp, _vp, _int, _sz, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize_rows": [_vp, _vp, _sz, _sz, _u32, _vp, _int, _vp],
     "qar_allreduce_simulated": [_vp, _int, _u32, _sz, _u32, _int, _vp, _vp, _vp, _u32, _vp, _u32, _vp],
+    "qar_quantize_blocks_e4m3": [_vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_reduce_quantized_e4m3": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_quantize_reduce_e4m3": [_vp, _int, _u32, _vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_ring_step_e4m3": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_dequantize_e4m3": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
     "qar_status_string": [_int],
     "qar_last_error": [],
 }
@@ -120,19 +125,34 @@ def _ptrs(ts: list[torch.Tensor]):
 # the calls
 
 
-def qar_quantize_blocks(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
-                        scales: torch.Tensor | None = None, stream=None):
-    """x (bf16/fp32, any shape, contiguous) -> (codes int8[n], scales fp32[n/block])."""
+# code formats: the C function suffix and the torch dtype that holds the codes
+_INT8 = ("", torch.int8)
+_E4M3 = ("_e4m3", torch.uint8)
+
+
+def _quantize(fmt, x, block, codes, scales, stream):
+    name = "qar_quantize_blocks" + fmt[0]
     _dev(x, "x")
     n = x.numel()
     if codes is None:
-        codes = torch.empty(n, dtype=torch.int8, device=x.device)
+        codes = torch.empty(n, dtype=fmt[1], device=x.device)
     if scales is None:
         scales = torch.empty(max(n // block, 1), dtype=torch.float32, device=x.device)
-    _check(lib().qar_quantize_blocks(x.data_ptr(), _dtype_code(x.dtype), n, block,
-                                     _dev(codes, "codes").data_ptr(), _dev(scales, "scales").data_ptr(),
-                                     _stream(stream)), "qar_quantize_blocks")
+    _check(getattr(lib(), name)(x.data_ptr(), _dtype_code(x.dtype), n, block, _dev(codes, "codes").data_ptr(),
+                                _dev(scales, "scales").data_ptr(), _stream(stream)), name)
     return codes, scales
+
+
+def qar_quantize_blocks(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
+                        scales: torch.Tensor | None = None, stream=None):
+    """x (bf16/fp32, any shape, contiguous) -> (codes int8[n], scales fp32[n/block])."""
+    return _quantize(_INT8, x, block, codes, scales, stream)
+
+
+def qar_quantize_blocks_e4m3(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None, stream=None):
+    """x (bf16/fp32) -> (FP8 E4M3 codes uint8[n], scales fp32[n/block])."""
+    return _quantize(_E4M3, x, block, codes, scales, stream)
 
 
 def _out_args(out: torch.Tensor | None):
@@ -142,11 +162,8 @@ def _out_args(out: torch.Tensor | None):
     return out.data_ptr(), _dtype_code(out.dtype)
 
 
-def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
-                         codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
-                         out: torch.Tensor | None = None, stream=None):
-    """One-shot N-way reduce of rank-ordered (codes, scales) -> (codes_out, scales_out);
-    ``out`` (optional bf16/fp32 tensor) receives the dequantized result."""
+def _reduce(fmt, codes, scales, block, codes_out, scales_out, out, stream):
+    name = "qar_reduce_quantized" + fmt[0]
     if len(codes) != len(scales) or not codes:
         raise ValueError("need one scales tensor per codes tensor, at least one rank")
     n = codes[0].numel()
@@ -154,15 +171,48 @@ def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], 
         _dev(c, "codes[r]"), _dev(s, "scales[r]")
     dev = codes[0].device
     if codes_out is None:
-        codes_out = torch.empty(n, dtype=torch.int8, device=dev)
+        codes_out = torch.empty(n, dtype=fmt[1], device=dev)
     if scales_out is None:
         scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
     optr, odt = _out_args(out)
     cp, sp = _ptrs(codes), _ptrs(scales)
-    _check(lib().qar_reduce_quantized(ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), len(codes), n, block,
-                                      _dev(codes_out, "codes_out").data_ptr(),
-                                      _dev(scales_out, "scales_out").data_ptr(), optr, odt,
-                                      _stream(stream)), "qar_reduce_quantized")
+    _check(getattr(lib(), name)(ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), len(codes), n, block,
+                                _dev(codes_out, "codes_out").data_ptr(), _dev(scales_out, "scales_out").data_ptr(),
+                                optr, odt, _stream(stream)), name)
+    return codes_out, scales_out
+
+
+def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
+                         codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, stream=None):
+    """One-shot N-way reduce of rank-ordered (codes, scales) -> (codes_out, scales_out);
+    ``out`` (optional bf16/fp32 tensor) receives the dequantized result."""
+    return _reduce(_INT8, codes, scales, block, codes_out, scales_out, out, stream)
+
+
+def qar_reduce_quantized_e4m3(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
+                              codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, stream=None):
+    """The one-shot reduce with FP8 E4M3 codes (uint8 tensors)."""
+    return _reduce(_E4M3, codes, scales, block, codes_out, scales_out, out, stream)
+
+
+def _quantize_reduce(fmt, x_own, own, codes, scales, block, codes_out, scales_out, out, stream):
+    name = "qar_quantize_reduce" + fmt[0]
+    if len(codes) != len(scales) or not codes:
+        raise ValueError("need one scales tensor per codes tensor, at least one rank")
+    _dev(x_own, "x_own")
+    n = x_own.numel()
+    dev = x_own.device
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=fmt[1], device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
+    optr, odt = _out_args(out)
+    cp, sp = _ptrs(codes), _ptrs(scales)
+    _check(getattr(lib(), name)(x_own.data_ptr(), _dtype_code(x_own.dtype), own, ctypes.cast(cp, _vp),
+                                ctypes.cast(sp, _vp), len(codes), n, block, _dev(codes_out, "codes_out").data_ptr(),
+                                _dev(scales_out, "scales_out").data_ptr(), optr, odt, _stream(stream)), name)
     return codes_out, scales_out
 
 
@@ -171,22 +221,14 @@ def qar_quantize_reduce(x_own: torch.Tensor, own: int, codes: list[torch.Tensor]
                         out: torch.Tensor | None = None, stream=None):
     """Quantize x_own into codes[own]/scales[own] and reduce all ranks in the
     same pass -> (codes_out, scales_out); ``out`` gets the dequantized result."""
-    if len(codes) != len(scales) or not codes:
-        raise ValueError("need one scales tensor per codes tensor, at least one rank")
-    _dev(x_own, "x_own")
-    n = x_own.numel()
-    dev = x_own.device
-    if codes_out is None:
-        codes_out = torch.empty(n, dtype=torch.int8, device=dev)
-    if scales_out is None:
-        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
-    optr, odt = _out_args(out)
-    cp, sp = _ptrs(codes), _ptrs(scales)
-    _check(lib().qar_quantize_reduce(x_own.data_ptr(), _dtype_code(x_own.dtype), own, ctypes.cast(cp, _vp),
-                                     ctypes.cast(sp, _vp), len(codes), n, block,
-                                     _dev(codes_out, "codes_out").data_ptr(), _dev(scales_out, "scales_out").data_ptr(),
-                                     optr, odt, _stream(stream)), "qar_quantize_reduce")
-    return codes_out, scales_out
+    return _quantize_reduce(_INT8, x_own, own, codes, scales, block, codes_out, scales_out, out, stream)
+
+
+def qar_quantize_reduce_e4m3(x_own: torch.Tensor, own: int, codes: list[torch.Tensor],
+                             scales: list[torch.Tensor], block: int, codes_out: torch.Tensor | None = None,
+                             scales_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None):
+    """The one-kernel step with FP8 E4M3 codes."""
+    return _quantize_reduce(_E4M3, x_own, own, codes, scales, block, codes_out, scales_out, out, stream)
 
 
 def qar_reduce_quantized_pipelined(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
@@ -212,32 +254,54 @@ def qar_reduce_quantized_pipelined(codes: list[torch.Tensor], scales: list[torch
     return codes_out, scales_out
 
 
+def _ring_step(fmt, codes_in, scales_in, local, block, codes_out, scales_out, stream):
+    name = "qar_ring_step" + fmt[0]
+    _dev(codes_in, "codes_in"), _dev(scales_in, "scales_in"), _dev(local, "local")
+    n = codes_in.numel()
+    if codes_out is None:
+        codes_out = torch.empty(n, dtype=fmt[1], device=codes_in.device)
+    if scales_out is None:
+        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=codes_in.device)
+    _check(getattr(lib(), name)(codes_in.data_ptr(), scales_in.data_ptr(), local.data_ptr(),
+                                _dtype_code(local.dtype), n, block, _dev(codes_out, "codes_out").data_ptr(),
+                                _dev(scales_out, "scales_out").data_ptr(), _stream(stream)), name)
+    return codes_out, scales_out
+
+
 def qar_ring_step(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
                   codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
     """quantize(dequantize(codes_in, scales_in) + local) -> (codes_out, scales_out).
     Pass codes_out=codes_in, scales_out=scales_in to work in place."""
-    _dev(codes_in, "codes_in"), _dev(scales_in, "scales_in"), _dev(local, "local")
-    n = codes_in.numel()
-    if codes_out is None:
-        codes_out = torch.empty(n, dtype=torch.int8, device=codes_in.device)
-    if scales_out is None:
-        scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=codes_in.device)
-    _check(lib().qar_ring_step(codes_in.data_ptr(), scales_in.data_ptr(), local.data_ptr(),
-                               _dtype_code(local.dtype), n, block, _dev(codes_out, "codes_out").data_ptr(),
-                               _dev(scales_out, "scales_out").data_ptr(), _stream(stream)), "qar_ring_step")
-    return codes_out, scales_out
+    return _ring_step(_INT8, codes_in, scales_in, local, block, codes_out, scales_out, stream)
+
+
+def qar_ring_step_e4m3(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
+                       codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
+    """The ring step with FP8 E4M3 codes."""
+    return _ring_step(_E4M3, codes_in, scales_in, local, block, codes_out, scales_out, stream)
+
+
+def _dequantize(fmt, codes, scales, block, out, out_dtype, stream):
+    name = "qar_dequantize" + fmt[0]
+    _dev(codes, "codes"), _dev(scales, "scales")
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(n, dtype=out_dtype, device=codes.device)
+    _check(getattr(lib(), name)(codes.data_ptr(), scales.data_ptr(), n, block, _dev(out, "out").data_ptr(),
+                                _dtype_code(out.dtype), _stream(stream)), name)
+    return out
 
 
 def qar_dequantize(codes: torch.Tensor, scales: torch.Tensor, block: int, out: torch.Tensor | None = None,
                    out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
     """codes, scales -> out (bf16 or fp32)."""
-    _dev(codes, "codes"), _dev(scales, "scales")
-    n = codes.numel()
-    if out is None:
-        out = torch.empty(n, dtype=out_dtype, device=codes.device)
-    _check(lib().qar_dequantize(codes.data_ptr(), scales.data_ptr(), n, block, _dev(out, "out").data_ptr(),
-                                _dtype_code(out.dtype), _stream(stream)), "qar_dequantize")
-    return out
+    return _dequantize(_INT8, codes, scales, block, out, out_dtype, stream)
+
+
+def qar_dequantize_e4m3(codes: torch.Tensor, scales: torch.Tensor, block: int, out: torch.Tensor | None = None,
+                        out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """FP8 E4M3 codes (uint8), scales -> out (bf16 or fp32)."""
+    return _dequantize(_E4M3, codes, scales, block, out, out_dtype, stream)
 
 
 def qar_reduce_unquantized(xs: list[torch.Tensor], out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

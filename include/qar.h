@@ -257,6 +257,44 @@ qar_status qar_ring_step_rows(const int8_t* codes_in, const float* scales_in, co
 qar_status qar_dequantize_rows(const int8_t* codes, const float* scales, size_t rows, size_t row_len,
                                uint32_t block, void* out, qar_dtype out_dtype, void* stream);
 
+/*
+ * FP8 E4M3 codes.  The same calls with 8-bit floating-point codes in place
+ * of int8 integers: the format the TACO page argues for ("TACO:
+ * Tensor-parallel Adaptive COmmunication compression", page summary,
+ * section "Why FP8?"), with the per-block scale of its "Dual-Scale
+ * quantization" section that brings the block into FP8's range Q_max (only
+ * that scale; no rotation).  E4M3 is the OCP format: sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals (m/8) * 2^-6, no infinity, codes
+ * 0x7F and 0xFF NaN (never produced), largest finite value 448.
+ *
+ *   scale  s   = absmax / 448            one IEEE binary32 division
+ *   code   c_i = 0x00 if s == 0; else the E4M3 value nearest to
+ *                clamp(x_i / s, -448, 448) (the correctly rounded binary32
+ *                quotient), ties to the even mantissa; the sign is kept, so
+ *                a negative quotient that rounds to zero gives 0x80 (-0)
+ *   value  y_i = e4m3(c_i) * s           one binary32 multiply
+ *
+ * Codes are uint8_t[n], one byte per element, in the same layout as the int8
+ * codes; scales, alignment, aliasing, streams and errors are exactly those of
+ * the int8 call of the same name.  The reduce, the one-kernel step and the
+ * ring step sum in binary32 in rank order and requantize with this
+ * quantizer; a sum is -0 only when every term is.
+ */
+qar_status qar_quantize_blocks_e4m3(const void* x, qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes,
+                                    float* scales, void* stream);
+qar_status qar_reduce_quantized_e4m3(const uint8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t n, uint32_t block, uint8_t* codes_out, float* scales_out, void* out,
+                                     qar_dtype out_dtype, void* stream);
+qar_status qar_quantize_reduce_e4m3(const void* x_own, qar_dtype dtype, uint32_t own, uint8_t* const* codes,
+                                    float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                                    uint8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                                    void* stream);
+qar_status qar_ring_step_e4m3(const uint8_t* codes_in, const float* scales_in, const void* local,
+                              qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes_out, float* scales_out,
+                              void* stream);
+qar_status qar_dequantize_e4m3(const uint8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                               qar_dtype out_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* qar_status_string(qar_status status);
 

@@ -314,20 +314,36 @@ static float e4m3_value(uint8_t c)
     return (c & 0x80) ? -mag : mag;
 }
 
+/* The non-negative finite E4M3 values in code order 0..126, which is
+ * increasing order; filled from e4m3_value() when the library is loaded. */
+static float e4m3_table[127];
+
+__attribute__((constructor)) static void e4m3_fill_table(void)
+{
+    for (unsigned c = 0; c < 127; c++)
+        e4m3_table[c] = e4m3_value((uint8_t)c);
+}
+
 /* The E4M3 code nearest to t, |t| <= 448, ties to the code whose mantissa
- * (lowest bit) is even.  The finite non-negative codes 0..126 are in
- * increasing order of value, so a linear walk finds the neighbours below
- * and above |t|; both distances are exact in binary64. */
+ * (lowest bit) is even.  Binary search in the ordered table for the largest
+ * value <= |t|, then the nearer of it and the next one; both distances are
+ * exact in binary64. */
 static uint8_t e4m3_nearest(float t)
 {
     uint8_t sign = signbit(t) ? 0x80 : 0x00;
     float a = fabsf(t);
-    unsigned c = 0;
-    while (c < 126 && e4m3_value((uint8_t)(c + 1)) <= a)
-        c++;
+    unsigned lo = 0, hi = 126;           /* invariant: table[lo] <= a */
+    while (lo < hi) {
+        unsigned mid = (lo + hi + 1) / 2;
+        if (e4m3_table[mid] <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    unsigned c = lo;
     if (c < 126) {
-        double below = (double)a - (double)e4m3_value((uint8_t)c);
-        double above = (double)e4m3_value((uint8_t)(c + 1)) - (double)a;
+        double below = (double)a - (double)e4m3_table[c];
+        double above = (double)e4m3_table[c + 1] - (double)a;
         if (above < below || (above == below && (c & 1u)))
             c++;
     }

@@ -3,6 +3,39 @@ generator and the oracle; bf16 travels as uint16 bit patterns)."""
 import numpy as np
 import torch
 
+from block_wise_int8_amd import synth
+
+TILE = 4096
+SUM_OUTLIER = 9.0e36     # 32 of them still sum below the largest binary32
+
+
+def ragged_n(block: int, tiles: int = 3) -> int:
+    """Several 4096-element tiles plus a tail of 5 blocks."""
+    return tiles * TILE + 5 * block
+
+
+def mixed_f32(seed: int, n: int, block: int, outlier: float = 3.0e38) -> np.ndarray:
+    """fp32 data with per-block magnitudes across the range plus special
+    blocks: all zero, signed zeros, constant, subnormal, one outlier.  Data
+    that is summed takes a smaller outlier so that no binary32 sum
+    overflows (the method is undefined for an infinite sum)."""
+    x = synth.wide_range_f32(seed, n, block, log2_span=50)
+    nb = n // block
+    rng = np.random.default_rng(seed + 1)
+    b = rng.permutation(nb)[:6] * block
+    x[b[0]:b[0] + block] = 0.0
+    x[b[1]:b[1] + block] = -0.0
+    x[b[1] + 3] = 1.0
+    x[b[2]:b[2] + block] = np.float32(-3.25)
+    x[b[3]:b[3] + block] = (rng.normal(0, 1, block) * 2.0 ** -140).astype(np.float32)
+    x[b[4]:b[4] + block] = (rng.normal(0, 1, block) * 2.0 ** -149).astype(np.float32)
+    x[b[5] + 7] = np.float32(outlier)
+    return x
+
+
+def mixed_bf16(seed: int, n: int, block: int, outlier: float = 3.0e38) -> np.ndarray:
+    return synth.f32_to_bf16_bits(mixed_f32(seed, n, block, outlier))
+
 
 def to_dev(a: np.ndarray, device="cuda:0") -> torch.Tensor:
     a = np.ascontiguousarray(a)

@@ -89,6 +89,24 @@ def test_quantize_reduce_validation(L):
         == qar.QAR_ERR_INVALID_ARG
 
 
+def test_e4m3_validation(L):
+    """The E4M3 calls share the int8 calls' checks."""
+    codes, scales = _arr(A, B_), _arr(C, D)
+    assert L.qar_quantize_blocks_e4m3(A, 0, 0, 256, B_, C, None) == qar.QAR_OK
+    assert L.qar_quantize_blocks_e4m3(A, 0, 256, 96, B_, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert L.qar_quantize_blocks_e4m3(A + 2, 0, 256, 256, B_, C, None) == qar.QAR_ERR_MISALIGNED
+    assert L.qar_quantize_blocks_e4m3(A, 0, 256, 256, A + 64, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_reduce_quantized_e4m3(codes, scales, 33, 256, 256, 0x50000, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_reduce_quantized_e4m3(codes, scales, 2, 256, 256, B_ + 16, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_quantize_reduce_e4m3(0x80000, 0, 2, codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0,
+                                      None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_ring_step_e4m3(A, C, 0x80000, 0, 256, 256, A, 0x60000, None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_dequantize_e4m3(A, C, 256, 256, A + 16, 0, None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_dequantize_e4m3(A, C, 256, 256, 0x80000, 5, None) == qar.QAR_ERR_UNSUPPORTED
+
+
 def test_pipelined_validation(L):
     p = L.qar_reduce_quantized_pipelined
     codes, scales = _arr(A, B_), _arr(C, D)
