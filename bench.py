@@ -340,6 +340,7 @@ def main() -> int:
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
+        result["e4m3_codes"] = e4m3_bench(qar, torch, synth, dev, args.skew)
         result["row_bounded"] = rows_bench(qar, torch, dev)
 
     if not args.no_cpu_baseline:
@@ -485,6 +486,74 @@ def prefill_bench(qar, torch, synth, dev, skew):
     res["reduce_only"] = _rate((N + 1) * qbytes, _loop_us(torch, fn2, nsets, 50))
     del sets
     torch.cuda.empty_cache()
+    return res
+
+
+def e4m3_bench(qar, torch, synth, dev, skew):
+    """FP8 E4M3 codes against int8 codes on the outlier and prefill recipes
+    (data drawn on the GPU): time of the quantize, the reduce without output
+    and the one-kernel step on the outlier workload, and for both workloads
+    the error of each format's result against the exact (fp64) sum of the
+    bf16 inputs."""
+    res = {"note": "error = dequantized fp32 result of the one-shot reduce minus the fp64 sum of the N bf16 "
+                   "inputs, over every element; rms relative to the mean |sum|"}
+    for key in ("outliers", "prefill"):
+        w = synth.WORKLOADS[key]
+        N, n, B = w.nranks, w.n, w.block
+        xs = [synth.device_rank(w, r, dev) for r in range(N)]
+        exact = torch.zeros(n, dtype=torch.float64, device=dev)
+        for x in xs:
+            exact += x.double()
+        mean_abs = exact.abs().mean().item()
+        errs = {}
+        for fmt, quant, red, deq in (("int8", qar.qar_quantize_blocks, qar.qar_reduce_quantized,
+                                      qar.qar_dequantize),
+                                     ("e4m3", qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3,
+                                      qar.qar_dequantize_e4m3)):
+            q = [quant(x, B) for x in xs]
+            rc, rs = red([c for c, _ in q], [s for _, s in q], B)
+            y = deq(rc, rs, B, out_dtype=torch.float32).double()
+            d = (y - exact)
+            errs[fmt] = {"rms_over_mean_abs_sum": round((d.square().mean().sqrt() / mean_abs).item(), 6),
+                         "max_abs": round(d.abs().max().item(), 6)}
+            del q, rc, rs, y, d
+        res[key] = {"workload": w.description, **errs,
+                    "rms_ratio_int8_over_e4m3": round(errs["int8"]["rms_over_mean_abs_sum"] /
+                                                      errs["e4m3"]["rms_over_mean_abs_sum"], 3)}
+        if key == "outliers":
+            nb = n // B
+            qbytes = n + 4 * nb
+            q = [qar.qar_quantize_blocks_e4m3(x, B) for x in xs]
+            nsets = 4
+            sets = []
+            for _ in range(nsets):
+                sets.append({"x": xs[0].clone(), "codes": _rank_block(torch, [c for c, _ in q], skew, dev),
+                             "scales": [s.clone() for _, s in q],
+                             "co": torch.empty(n, dtype=torch.uint8, device=dev),
+                             "so": torch.empty(nb, dtype=torch.float32, device=dev),
+                             "out": torch.empty(n, dtype=torch.bfloat16, device=dev)})
+            del q
+
+            def fq(i):
+                st = sets[i]
+                qar.qar_quantize_blocks_e4m3(st["x"], B, st["codes"][0], st["scales"][0])
+
+            def fr(i):
+                st = sets[i]
+                qar.qar_reduce_quantized_e4m3(st["codes"], st["scales"], B, st["co"], st["so"])
+
+            def fs(i):
+                st = sets[i]
+                qar.qar_quantize_reduce_e4m3(st["x"], 0, st["codes"], st["scales"], B, st["co"], st["so"],
+                                             out=st["out"])
+            res["timing_outliers"] = {
+                "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 100)),
+                "reduce_no_out": _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 100)),
+                "one_kernel_step": _rate(2 * n + (N + 1) * qbytes + 2 * n, _loop_us(torch, fs, nsets, 100)),
+            }
+            del sets
+        del xs, exact
+        torch.cuda.empty_cache()
     return res
 
 
