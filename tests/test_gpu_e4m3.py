@@ -79,6 +79,32 @@ def test_quantize_e4m3_every_rounding_boundary(oracle_lib):
     assert_same_codes(_codes(codes), wc, "E4M3 codes at rounding boundaries")
 
 
+def test_quantize_e4m3_every_fp32_rounding_class(oracle_lib):
+    """Blocks led by 448 have scale 1, so the quotient is x itself: every
+    binary32 exponent up to 448's, both signs, each value of the top 4
+    mantissa bits (the 3 an E4M3 value keeps and the rounding bit), with
+    the 19 bits below zero, lowest set, all set, or random."""
+    rng = np.random.default_rng(97)
+    e = np.arange(0, 136, dtype=np.uint32)[:, None, None]          # biased exponents of 0 .. 2^8
+    top = np.arange(16, dtype=np.uint32)[None, :, None]
+    low = np.stack([np.zeros(136 * 16, np.uint32), np.ones(136 * 16, np.uint32),
+                    np.full(136 * 16, (1 << 19) - 1, np.uint32),
+                    rng.integers(0, 1 << 19, 136 * 16).astype(np.uint32)], axis=1).reshape(136, 16, 4)
+    bits = (e << 23) | (top << 19) | low
+    bits = np.concatenate([bits.reshape(-1), bits.reshape(-1) | np.uint32(0x80000000)])
+    x = bits.view(np.float32)
+    x = x[np.abs(x) <= 448.0]
+    per = 63
+    x = np.concatenate([x, np.zeros((-x.size) % per, np.float32)]).reshape(-1, per)
+    x = np.concatenate([np.full((x.shape[0], 1), np.float32(448.0)), x], axis=1).reshape(-1)
+    say(f"e4m3 fp32 rounding classes n={x.size}")
+    codes, scales = qar.qar_quantize_blocks_e4m3(to_dev(x), 64)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.quantize_e4m3(x, 64)
+    assert np.all(ws == 1.0)
+    assert_same_codes(_codes(codes), wc, "E4M3 codes of every fp32 rounding class")
+
+
 def test_quantize_e4m3_every_bf16_against_many_scales(oracle_lib):
     """Every finite bf16 x against 128 absmax values spread over the bf16
     range (inexact scales, so the quotient's rounding matters too)."""

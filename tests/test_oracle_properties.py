@@ -69,3 +69,36 @@ def test_ring_step_any_input(oracle_lib, block, nblocks, data):
                              [Fraction(float(v)) for v in local], block)
     assert list(oc.astype(int)) == bc
     assert [Fraction(float(v)) for v in os_] == bs
+
+
+# ----------------------------------------------------------------------------
+# FP8 E4M3 codes
+
+
+def _neg_zero(x) -> list[bool]:
+    return [bool(v == 0 and np.signbit(v)) for v in np.asarray(x, np.float32)]
+
+
+@COMMON
+@given(st.lists(FINITE_F32, min_size=1, max_size=24), st.integers(1, 9))
+def test_quantize_e4m3_fp32_any_bits(oracle_lib, bits, block):
+    x = _f32(bits)
+    codes, scales = oracle_lib.quantize_e4m3(x, block)
+    bc, bs = brute.quantize_e4m3([Fraction(float(v)) for v in x], block, _neg_zero(x))
+    assert list(codes.astype(int)) == bc
+    assert [Fraction(float(s)) for s in scales] == bs
+
+
+@COMMON
+@given(st.integers(1, 5), st.integers(1, 6), st.integers(1, 3), st.data())
+def test_reduce_e4m3_any_codes(oracle_lib, nranks, block, nblocks, data):
+    n = block * nblocks - data.draw(st.integers(0, block - 1))
+    finite = st.integers(0, 255).filter(lambda c: c not in (0x7F, 0xFF))
+    codes = [np.array(data.draw(st.lists(finite, min_size=n, max_size=n)), np.uint8) for _ in range(nranks)]
+    scales = [np.array(data.draw(st.lists(SCALE, min_size=nblocks, max_size=nblocks)), np.float32)
+              for _ in range(nranks)]
+    oc, os_ = oracle_lib.reduce_e4m3(codes, scales, block)
+    bc, bs = brute.reduce_e4m3([list(c.astype(int)) for c in codes],
+                               [[Fraction(float(v)) for v in s] for s in scales], block)
+    assert list(oc.astype(int)) == bc
+    assert [Fraction(float(v)) for v in os_] == bs
