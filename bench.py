@@ -91,9 +91,9 @@ def parse():
 # the outlier workload's kernels; N ranks, n elements, block B, bf16 in/out
 def _counter_kernels(N, n, B):
     qb = n + 4 * (n // B)
-    return [("k_quantize_reduce<", 2 * n + (N - 1) * qb, 2 * qb + 2 * n),
-            ("k_quantize<", 2 * n, qb),
-            ("k_reduce<", N * qb, qb + 2 * n)]
+    return [("k_quantize_reduce<256, 0, unsigned short, qar::Int8Codes>", 2 * n + (N - 1) * qb, 2 * qb + 2 * n),
+            ("k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", 2 * n, qb),
+            ("k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", N * qb, qb + 2 * n)]
 
 
 def summarize_counters(d: str) -> int:
@@ -121,7 +121,7 @@ def summarize_counters(d: str) -> int:
         f, nd = mean_kib("pmc_fetch", name)
         wr, _ = mean_kib("pmc_write", name)
         rd, wb = int(f * ff * 1024), int(wr * fw * 1024)
-        rows[name.rstrip("<")] = {"dispatches": nd, "fetch_kib_raw_mean": round(f, 2), "write_kib_raw_mean": round(wr, 2),
+        rows[name.split("<")[0]] = {"dispatches": nd, "fetch_kib_raw_mean": round(f, 2), "write_kib_raw_mean": round(wr, 2),
                                   "hbm_read_bytes": rd, "hbm_write_bytes": wb, "algorithmic_read_bytes": alg_r,
                                   "algorithmic_write_bytes": alg_w,
                                   "traffic_over_algorithmic": round((rd + wb) / (alg_r + alg_w), 4)}
