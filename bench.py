@@ -765,7 +765,14 @@ def cpu_baseline(args, np, w, host, set0, torch):
     same = (bool(np.array_equal(gpu_codes, oc)) and bool(np.array_equal(gpu_out.view(y.dtype), y))
             and bool(np.array_equal(own_codes, c0)))
     payload = w.nranks * w.n * 2
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(payload / dtT / 1e9, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"the whole workload, {reps} repetitions of the step (quantize own buffer, reduce "
                       f"{w.nranks} ranks, dequantize) on {T} host threads, each on its own block range; "
                       f"{dtT:.3f} s per step",
