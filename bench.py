@@ -398,6 +398,18 @@ def _loop_us(torch, fn, count, reps, warmup=3):
     return _segmented_us(torch, lambda i: fn(i % count), reps)
 
 
+def _graph_of(torch, fn):
+    """fn() captured in a HIP graph (torch.cuda.graph), after one eager call
+    that creates the library's cached events."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def _rate(nbytes, us):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
@@ -594,6 +606,15 @@ def pipelined_bench(qar, torch, synth, dev, skew):
         r = _rate(nbytes, _loop_us(torch, fn, nsets, 20, warmup=30))
         r.update({"nchunks": nchunks, "nstreams": nstr, "call": "qar_reduce_quantized_pipelined"})
         sweep.append(r)
+    # the same chunked schedules captured once in a HIP graph and replayed:
+    # no host launch work and no queue switches on the host side
+    for nchunks, nstr in ((4, 4), (16, 4), (64, 4)):
+        graphs = [_graph_of(torch, lambda i=i, nchunks=nchunks, nstr=nstr: qar.qar_reduce_quantized_pipelined(
+            sets[i][0], sets[i][1], B, nchunks, streams[:nstr], sets[i][2], sets[i][3])) for i in range(nsets)]
+        r = _rate(nbytes, _loop_us(torch, lambda i: graphs[i].replay(), nsets, 20, warmup=5))
+        r.update({"nchunks": nchunks, "nstreams": nstr, "call": "qar_reduce_quantized_pipelined, HIP graph replay"})
+        sweep.append(r)
+        del graphs
     del sets
     torch.cuda.empty_cache()
     best = min(sweep, key=lambda x: x["avg_us"])
@@ -668,6 +689,12 @@ def allreduce_bench(qar, torch, synth, dev):
             us = _loop_us(torch, fn, 1, 20, warmup=30)
             rows.append({"schedule": sched, "nchunks": nchunks, "nstreams": nstr, "avg_us": round(us, 2),
                          "error": err_stats(out)})
+            if nstr > 1:
+                g = _graph_of(torch, lambda: fn(0))
+                gus = _loop_us(torch, lambda i: g.replay(), 1, 20, warmup=5)
+                rows.append({"schedule": sched, "nchunks": nchunks, "nstreams": nstr, "hip_graph": True,
+                             "avg_us": round(gus, 2), "error": err_stats(out)})
+                del g
     def fb(i):
         qar.qar_reduce_unquantized(xs, out=out)
     us = _loop_us(torch, fb, 1, 50)
