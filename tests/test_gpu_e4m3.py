@@ -300,3 +300,37 @@ def test_e4m3_workload(oracle_lib, key):
     err = np.abs(deq - exact)
     assert np.all(err <= bnd), f"{key}: E4M3 bound violated, worst ratio {np.max(err / bnd)}"
     say(f"e4m3 {key}: max err/bound {np.max(err / bnd):.3f}")
+
+
+def test_e4m3_beyond_2_pow_31_elements(oracle_lib):
+    """E4M3 quantize, dequantize and the one-kernel step (N = 2) at n above
+    2**31, checked against the oracle on sampled blocks and the last ones."""
+    from gpu_util import TILE
+    block = 256
+    n = (1 << 31) + 3 * TILE + 7 * block
+    say(f"e4m3 large n={n}")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(77)
+    x0 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 1.0, generator=g)
+    x1 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 2.0, generator=g)
+    c1, s1 = qar.qar_quantize_blocks_e4m3(x1, block)
+    y1 = qar.qar_dequantize_e4m3(c1, s1, block, out_dtype=torch.bfloat16)
+    c0 = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    s0 = torch.empty(n // block, dtype=torch.float32, device="cuda:0")
+    fc, fs = qar.qar_quantize_reduce_e4m3(x0, 0, [c0, c1], [s0, s1], block)
+    torch.cuda.synchronize()
+    nb = n // block
+    rng = np.random.default_rng(8)
+    picks = np.concatenate([rng.choice(nb, 2000, replace=False), np.arange(nb - 40, nb)])
+    pk = torch.from_numpy(picks).cuda()
+    idx = torch.from_numpy((picks[:, None] * block + np.arange(block)).reshape(-1)).cuda()
+    q = [oracle_lib.quantize_e4m3(to_host(x[idx]), block) for x in (x0, x1)]
+    assert_same_codes(_codes(c1[idx]), q[1][0], "codes")
+    assert_same_f32(to_host(s1[pk]), q[1][1], "scales")
+    assert_same_bits16(to_host(y1[idx]), oracle_lib.dequantize_e4m3(q[1][0], q[1][1], block, "bf16"), "dequantized")
+    wc, ws = oracle_lib.reduce_e4m3([a for a, _ in q], [b for _, b in q], block)
+    assert_same_codes(_codes(c0[idx]), q[0][0], "own codes")
+    assert_same_codes(_codes(fc[idx]), wc, "step codes")
+    assert_same_f32(to_host(fs[pk]), ws, "step scales")
+    del x0, x1, c0, c1, s0, s1, y1, fc, fs
+    torch.cuda.empty_cache()

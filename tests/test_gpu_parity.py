@@ -423,3 +423,36 @@ def test_beyond_2_pow_31_elements(oracle_lib):
     assert_same_bits16(to_host(y[idx]), oracle_lib.dequantize(wc, ws, block, "bf16"), "dequantized")
     del x, codes, scales, y
     torch.cuda.empty_cache()
+
+
+def test_reduce_beyond_2_pow_31_elements(oracle_lib):
+    """The one-kernel step and the plain reduce with N = 2 at n above 2**31,
+    checked against the oracle on sampled blocks and the last blocks."""
+    block = 128
+    n = (1 << 31) + 5 * TILE + 3 * block
+    say(f"large reduce n={n}")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(321)
+    x0 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 1.0, generator=g)
+    x1 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 3.0, generator=g)
+    c1, s1 = qar.qar_quantize_blocks(x1, block)
+    c0 = torch.empty(n, dtype=torch.int8, device="cuda:0")
+    s0 = torch.empty(n // block, dtype=torch.float32, device="cuda:0")
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    fc, fs = qar.qar_quantize_reduce(x0, 0, [c0, c1], [s0, s1], block, out=out)
+    rc, rs = qar.qar_reduce_quantized([c0, c1], [s0, s1], block)
+    torch.cuda.synchronize()
+    nb = n // block
+    rng = np.random.default_rng(6)
+    picks = np.concatenate([rng.choice(nb, 2000, replace=False), np.arange(nb - 40, nb)])
+    pk = torch.from_numpy(picks).cuda()
+    idx = torch.from_numpy((picks[:, None] * block + np.arange(block)).reshape(-1)).cuda()
+    q = [oracle_lib.quantize(to_host(x[idx]), block) for x in (x0, x1)]
+    wc, ws = oracle_lib.reduce([a for a, _ in q], [b for _, b in q], block)
+    assert_same_codes(to_host(c0[idx]), q[0][0], "own codes")
+    for c, s, what in ((fc, fs, "one-kernel step"), (rc, rs, "reduce")):
+        assert_same_codes(to_host(c[idx]), wc, f"{what} codes")
+        assert_same_f32(to_host(s[pk]), ws, f"{what} scales")
+    assert_same_bits16(to_host(out[idx]), oracle_lib.dequantize(wc, ws, block, "bf16"), "out")
+    del x0, x1, c0, c1, s0, s1, out, fc, fs, rc, rs
+    torch.cuda.empty_cache()
