@@ -258,13 +258,13 @@ def main() -> int:
     # each kernel of the step on its own: R launches back to back over the
     # rotated sets, events only at 5 segment boundaries (events between
     # kernels would add their own overhead to every launch)
-    def per_launch_us(fn, reps):
+    def per_launch_us(fn, reps, with_min=False):
         for i in range(3):
             fn(sets[i % len(sets)])
-        return _segmented_us(torch, lambda i: fn(sets[i % len(sets)]), reps)
+        return _segmented_us(torch, lambda i: fn(sets[i % len(sets)]), reps, with_min=with_min)
 
     reps = max(args.steps, 50)
-    f_us = per_launch_us(fused_step, reps)
+    f_us, f_min = per_launch_us(fused_step, reps, with_min=True)
     q_us = per_launch_us(quantize_own, reps)
     r_us = per_launch_us(reduce_fused, reps)
 
@@ -272,6 +272,9 @@ def main() -> int:
         quantize_own(st)
         reduce_fused(st)
     two_us = per_launch_us(two_kernels, reps)
+    # (stream=None: inside the capture the current stream is the capturing one)
+    q_graph = _graph_loop_us(torch, lambda i: qar.qar_quantize_blocks(sets[i]["x"], B, sets[i]["codes"][0],
+                                                                      sets[i]["scales"][0]), len(sets))
 
     payload = N * n * 2
     value = payload / (ms_per_step * 1e-3) / 1e9
@@ -315,13 +318,15 @@ def main() -> int:
             "traffic": measured_traffic(w.key),
             "algorithmic_bytes_per_launch": fused_bytes,
             "avg_launch_us": round(f_us, 3),
+            "min_launch_us": round(f_min, 3),
             "timing": f"{reps} back-to-back launches over the rotated sets, median of 5 event-bracketed segments",
         },
         "kernels": {
             "k_quantize_reduce (the step)": {"avg_us": round(f_us, 3), "bytes": fused_bytes,
                                              "GBps": round(achieved, 1)},
             "k_quantize": {"avg_us": round(q_us, 3), "bytes": quant_bytes,
-                           "GBps": round(quant_bytes / (q_us * 1e-6) / 1e9, 1)},
+                           "GBps": round(quant_bytes / (q_us * 1e-6) / 1e9, 1),
+                           "graph_replay": _rate(quant_bytes, q_graph)},
             "k_reduce (bf16 out)": {"avg_us": round(r_us, 3), "bytes": reduce_bytes,
                                     "GBps": round(reduce_bytes / (r_us * 1e-6) / 1e9, 1)},
         },
@@ -341,6 +346,7 @@ def main() -> int:
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
         result["e4m3_codes"] = e4m3_bench(qar, torch, synth, dev, args.skew)
+        result["tiny"] = tiny_bench(qar, torch, synth, dev)
         result["row_bounded"] = rows_bench(qar, torch, dev)
 
     if not args.no_cpu_baseline:
@@ -359,21 +365,21 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
     def fn(i):
         st = sets[i % len(sets)]
         qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"], stream=stream)
-    us = _loop_us(torch, fn, len(sets), reps, warmup=5)
+    us, us_min = _loop_us(torch, fn, len(sets), reps, warmup=5, with_min=True)
     nbytes = (N + 1) * qbytes
-    return {"avg_us": round(us, 3), "algorithmic_bytes": nbytes,
+    return {"avg_us": round(us, 3), "min_us": round(us_min, 3), "algorithmic_bytes": nbytes,
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "payload_GBps": round(N * n * 2 / (us * 1e-6) / 1e9, 1),
             "note": "back-to-back launches over rotated buffer sets, out=NULL"}
 
 
-def _segmented_us(torch, fn, reps, segments=5):
+def _segmented_us(torch, fn, reps, segments=5, with_min=False):
     """fn(i) for i in range(reps) back to back on the current stream, with
     an event at each of `segments` boundaries (no synchronisation between
     them).  Returns the median over segments of the average time per call,
     so a host-side pause that lets the GPU idle in one segment does not
-    count."""
+    count (and the fastest segment's, with_min=True)."""
     stream = torch.cuda.current_stream()
     per = max(1, reps // segments)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(segments + 1)]
@@ -387,15 +393,16 @@ def _segmented_us(torch, fn, reps, segments=5):
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     seg = sorted(ev[k].elapsed_time(ev[k + 1]) / per * 1e3 for k in range(segments))
-    return seg[len(seg) // 2]
+    return (seg[len(seg) // 2], seg[0]) if with_min else seg[len(seg) // 2]
 
 
-def _loop_us(torch, fn, count, reps, warmup=3):
+def _loop_us(torch, fn, count, reps, warmup=3, with_min=False):
     """Time per fn(i) over reps back-to-back launches (i cycles over
-    `count` buffer sets), median of 5 event-bracketed segments."""
+    `count` buffer sets), median of 5 event-bracketed segments (and the
+    fastest segment's, with_min=True)."""
     for i in range(warmup):
         fn(i % count)
-    return _segmented_us(torch, lambda i: fn(i % count), reps)
+    return _segmented_us(torch, lambda i: fn(i % count), reps, with_min=with_min)
 
 
 def _graph_of(torch, fn):
@@ -410,10 +417,37 @@ def _graph_of(torch, fn):
     return g
 
 
+def _graph_loop_us(torch, fn, count, per_graph=None, reps=8):
+    """Time per fn(i) with the host out of the loop: `per_graph` calls
+    (i = 0, 1, ... cycling over `count` buffer sets) captured in one HIP
+    graph, the graph replayed back to back; median and fastest of 5
+    event-bracketed segments of `reps` replays, divided by the calls per
+    replay.  For kernels short enough that the binding's per-call host work
+    (a few microseconds of Python and ctypes) would otherwise set the pace."""
+    per_graph = per_graph or max(count, 16)
+    for i in range(3):
+        fn(i % count)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i % count)
+    g.replay()
+    torch.cuda.synchronize()
+    med, mn = _segmented_us(torch, lambda i: g.replay(), 5 * reps, with_min=True)
+    del g
+    return med / per_graph, mn / per_graph
+
+
 def _rate(nbytes, us):
+    """us: median time per call, or (median, min) as _loop_us(..., with_min=True) returns."""
+    us, us_min = us if isinstance(us, tuple) else (us, None)
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    r = {"avg_us": round(us, 3), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
+         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if us_min is not None:
+        r["min_us"] = round(us_min, 3)
+    return r
 
 
 def _rank_block(torch, tensors, skew, dev):
@@ -437,7 +471,9 @@ def dequantize_bench(qar, torch, sets, B, n, qbytes):
     def fn(i):
         st = sets[i]
         qar.qar_dequantize(st["codes_out"], st["scales_out"], B, out=outs[i])
-    return _rate(qbytes + 2 * n, _loop_us(torch, fn, len(sets), 100))
+    res = _rate(qbytes + 2 * n, _loop_us(torch, fn, len(sets), 100, with_min=True))
+    res["graph_replay"] = _rate(qbytes + 2 * n, _graph_loop_us(torch, fn, len(sets)))
+    return res
 
 
 def comparator_bench(qar, torch, synth, w, dev, skew, reduce_only_us, step_us):
@@ -489,13 +525,13 @@ def prefill_bench(qar, torch, synth, dev, skew):
         c, s, co, so, out = sets[i]
         qar.qar_reduce_quantized(c, s, B, co, so, out=out)
     qbytes = n + 4 * nb
-    res = _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fn, nsets, 50))
+    res = _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fn, nsets, 50, with_min=True))
     res["workload"] = w.description + ", fused bf16 out"
 
     def fn2(i):
         c, s, co, so, out = sets[i]
         qar.qar_reduce_quantized(c, s, B, co, so)
-    res["reduce_only"] = _rate((N + 1) * qbytes, _loop_us(torch, fn2, nsets, 50))
+    res["reduce_only"] = _rate((N + 1) * qbytes, _loop_us(torch, fn2, nsets, 50, with_min=True))
     del sets
     torch.cuda.empty_cache()
     return res
@@ -560,6 +596,7 @@ def e4m3_bench(qar, torch, synth, dev, skew):
                                              out=st["out"])
             res["timing_outliers"] = {
                 "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 100)),
+                "quantize_graph_replay": _rate(2 * n + qbytes, _graph_loop_us(torch, fq, nsets)),
                 "reduce_no_out": _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 100)),
                 "one_kernel_step": _rate(2 * n + (N + 1) * qbytes + 2 * n, _loop_us(torch, fs, nsets, 100)),
             }
@@ -567,6 +604,32 @@ def e4m3_bench(qar, torch, synth, dev, skew):
         del xs, exact
         torch.cuda.empty_cache()
     return res
+
+
+def tiny_bench(qar, torch, synth, dev):
+    """The tiny workload (N=4 x 4,096 bf16, block 128): launch-latency
+    bound, data warm in cache; time per call of the reduce with bf16 out and
+    of the one-kernel step."""
+    w = synth.WORKLOADS["tiny"]
+    N, n, B = w.nranks, w.n, w.block
+    xs = [synth.device_rank(w, r, dev) for r in range(N)]
+    q = [qar.qar_quantize_blocks(x, B) for x in xs]
+    c, s = [a for a, _ in q], [b for _, b in q]
+    co, so = torch.empty_like(c[0]), torch.empty_like(s[0])
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    qbytes = n + 4 * (n // B)
+    r = _rate((N + 1) * qbytes + 2 * n,
+              _loop_us(torch, lambda i: qar.qar_reduce_quantized(c, s, B, co, so, out=out), 1, 200, 10, True))
+    st = _rate(2 * n + (N + 1) * qbytes + 2 * n,
+               _loop_us(torch, lambda i: qar.qar_quantize_reduce(xs[0], 0, c, s, B, co, so, out=out), 1, 200, 10,
+                        True))
+    r["graph_replay"] = _rate((N + 1) * qbytes + 2 * n, _graph_loop_us(
+        torch, lambda i: qar.qar_reduce_quantized(c, s, B, co, so, out=out), 1, per_graph=64))
+    st["graph_replay"] = _rate(2 * n + (N + 1) * qbytes + 2 * n, _graph_loop_us(
+        torch, lambda i: qar.qar_quantize_reduce(xs[0], 0, c, s, B, co, so, out=out), 1, per_graph=64))
+    return {"workload": w.description + " (warm: fits in cache)", "reduce_bf16_out": r, "one_kernel_step": st,
+            "note": "eager: one Python call per launch, so the binding's host work sets the pace; graph_replay: "
+                    "64 calls captured in one HIP graph, time per call"}
 
 
 def pipelined_bench(qar, torch, synth, dev, skew):
@@ -594,7 +657,7 @@ def pipelined_bench(qar, torch, synth, dev, skew):
     def one(i):
         c, s, co, so = sets[i]
         qar.qar_reduce_quantized(c, s, B, co, so)
-    r = _rate(nbytes, _loop_us(torch, one, nsets, 20))
+    r = _rate(nbytes, _loop_us(torch, one, nsets, 20, with_min=True))
     r.update({"nchunks": 1, "nstreams": 0, "call": "qar_reduce_quantized"})
     sweep.append(r)
     for nchunks, nstr in ((1, 1), (4, 4), (16, 4), (64, 4), (16, 1)):
@@ -718,24 +781,13 @@ def ring_bench(qar, torch, np, synth, dev):
     c0, s0 = qar.qar_quantize_blocks(x0, B)
     loc = torch.from_numpy(host[1].view(np.int16)).to(dev).view(torch.bfloat16)
     sets = [(c0.clone(), s0.clone(), loc.clone(), torch.empty_like(c0), torch.empty_like(s0)) for _ in range(S)]
-    stream = torch.cuda.current_stream()
-    for i in range(5):
-        c, s, l, co, so = sets[i % S]
-        qar.qar_ring_step(c, s, l, B, co, so, stream=stream)
-    reps = 200
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(reps):
-        c, s, l, co, so = sets[i % S]
-        qar.qar_ring_step(c, s, l, B, co, so, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
-    nbytes = 2 * (n + 4 * nb) + 2 * n
-    return {"workload": w.description, "avg_us": round(us, 3), "algorithmic_bytes": nbytes,
-            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    def fn(i):
+        c, s, l, co, so = sets[i]
+        qar.qar_ring_step(c, s, l, B, co, so)
+    res = _rate(2 * (n + 4 * nb) + 2 * n, _loop_us(torch, fn, S, 200, warmup=5, with_min=True))
+    res["graph_replay"] = _rate(2 * (n + 4 * nb) + 2 * n, _graph_loop_us(torch, fn, S, reps=4))
+    res["workload"] = w.description
+    return res
 
 
 def _cpu_threads() -> int:
