@@ -182,3 +182,47 @@ def test_rows_validation(L):
         qar.QAR_ERR_MISALIGNED
     g = L.qar_ring_step_rows
     assert g(A, C, B_, qar.QAR_BF16, 3, 100, 256, A, D, None) == qar.QAR_ERR_INVALID_ARG     # half in place
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "qar.h"
+
+/* A plain C99 caller: argument checks return before any HIP call, so this
+   runs without a GPU. */
+int main(void) {
+    int8_t* codes[2] = {(int8_t*)0x10000, (int8_t*)0x20000};
+    float* scales[2] = {(float*)0x30000, (float*)0x40000};
+    if (qar_quantize_blocks((const void*)0x10000, QAR_BF16, 0, 256, codes[0], scales[0], NULL) != QAR_OK) return 1;
+    if (qar_quantize_blocks((const void*)0x10000, QAR_BF16, 256, 100, codes[0], scales[0], NULL)
+        != QAR_ERR_UNSUPPORTED) return 2;
+    if (qar_reduce_quantized((const int8_t* const*)codes, (const float* const*)scales, 0, 256, 256,
+                             (int8_t*)0x50000, (float*)0x60000, NULL, QAR_BF16, NULL) != QAR_ERR_INVALID_ARG) return 3;
+    if (qar_quantize_reduce((const void*)0x80000, QAR_BF16, 5, codes, scales, 2, 256, 256, (int8_t*)0x50000,
+                            (float*)0x60000, NULL, QAR_BF16, NULL) != QAR_ERR_INVALID_ARG) return 4;
+    if (qar_dequantize_e4m3((const uint8_t*)0x10001, (const float*)0x30000, 256, 256, (void*)0x80000, QAR_F32,
+                            NULL) != QAR_ERR_MISALIGNED) return 5;
+    if (strcmp(qar_status_string(QAR_ERR_MISALIGNED), "misaligned pointer") != 0) return 6;
+    printf("%s\n", qar_status_string(QAR_OK));
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/qar.h compiles as C99 with warnings as errors, and a C program
+    links against libqar.so and gets the documented statuses."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(qar.LIBRARY)
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(root, "include"),
+                    str(src), "-o", str(exe), "-L", lib_dir, "-lqar", f"-Wl,-rpath,{lib_dir}",
+                    "-Wl,-rpath-link,/opt/rocm/lib"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == "ok"
