@@ -80,6 +80,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip the reduce-only and ring-step lines")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run 8 device-to-device copies of this many MiB (counter calibration) and exit")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the step: the reduce (no output) and the one-kernel step over rank counts "
+                        "and block sizes, one JSON line per point")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="no GPU: read the rocprofv3 --pmc CSVs of the four counter passes under DIR "
                         "(pmc_copy_fetch, pmc_copy_write, pmc_fetch, pmc_write) and write the traffic summary "
@@ -158,6 +161,8 @@ def main() -> int:
         return 1
     qar.lib()
     dev = torch.device("cuda:0")
+    if args.sweep:
+        return sweep(qar, torch, synth, dev, args.skew)
     if args.copy_probe_mib:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of these
         # dispatches calibrate the counters (bytes read = bytes written =
@@ -353,6 +358,45 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(args, np, w, host, sets[0], torch)
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def sweep(qar, torch, synth, dev, skew) -> int:
+    """The reduce without output and the one-kernel step (bf16 in and out)
+    on the outlier recipe (drawn on the GPU), n = 16,777,216 per rank, over
+    N in {2, 4, 8, 16, 32} at B = 256 and B in {64, 128} at N = 8; buffer
+    sets rotated so that at least 1 GiB is touched between reuses."""
+    w0 = synth.WORKLOADS["outliers"]
+    n = w0.n
+    x = [synth.device_rank(w0, r, dev) for r in range(32)]
+    for N, B in [(2, 256), (4, 256), (8, 256), (16, 256), (32, 256), (8, 64), (8, 128)]:
+        nb = n // B
+        qbytes = n + 4 * nb
+        q = [qar.qar_quantize_blocks(x[r], B) for r in range(N)]
+        per_set = (N + 2) * qbytes + 4 * n
+        nsets = max(2, -(-(1 << 30) // per_set))
+        sets = []
+        for _ in range(nsets):
+            sets.append({"x": x[0].clone(), "c": _rank_block(torch, [c for c, _ in q], skew, dev),
+                         "s": [s.clone() for _, s in q], "co": torch.empty(n, dtype=torch.int8, device=dev),
+                         "so": torch.empty(nb, dtype=torch.float32, device=dev),
+                         "out": torch.empty(n, dtype=torch.bfloat16, device=dev)})
+        del q
+
+        def fr(i):
+            st = sets[i]
+            qar.qar_reduce_quantized(st["c"], st["s"], B, st["co"], st["so"])
+
+        def fs(i):
+            st = sets[i]
+            qar.qar_quantize_reduce(st["x"], 0, st["c"], st["s"], B, st["co"], st["so"], out=st["out"])
+        red = _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 60, warmup=5, with_min=True))
+        step = _rate(2 * n + (N + 1) * qbytes + 2 * n, _loop_us(torch, fs, nsets, 60, warmup=5, with_min=True))
+        print(json.dumps({"nranks": N, "block": B, "elements_per_rank": n, "buffer_sets": nsets,
+                          "reduce_no_out": red, "one_kernel_step_bf16_out": step,
+                          "step_payload_GBps": round(N * n * 2 / (step["avg_us"] * 1e-6) / 1e9, 1)}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
     return 0
 
 
