@@ -446,16 +446,24 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
         const auto xin = [&](uint32_t r) { return (const void*)((const char*)x[r] + e0 * eb); };
         void* const oc = (void*)((char*)out + e0 * eb);
         if (schedule == QAR_SCHEDULE_ONE_SHOT) {
+            // ranks 0..N-2 quantized on their own; the last rank's quantize
+            // runs inside the reduce (one launch and one re-read fewer); the
+            // result replaces rank 0's codes, which each lane reads first
             qar::RankPtrs rp;
             memset(&rp, 0, sizeof rp);
-            for (uint32_t r = 0; e == hipSuccess && r < nranks; ++r) {
-                e = qar::launch_quantize(xin(r), kind, cn, (int)block, codes_work[r] + e0, scales_work[r] + b0, cs);
+            const uint32_t last = nranks - 1;
+            for (uint32_t r = 0; r < nranks; ++r) {
                 rp.codes[r] = codes_work[r] + e0;
                 rp.scales[r] = scales_work[r] + b0;
             }
-            if (e == hipSuccess)
-                e = qar::launch_reduce(rp, (int)nranks, cn, (int)block, codes_work[0] + e0, scales_work[0] + b0, oc,
-                                       okind, cs);
+            for (uint32_t r = 0; e == hipSuccess && r < (nranks > 1 ? last : nranks); ++r)
+                e = qar::launch_quantize(xin(r), kind, cn, (int)block, codes_work[r] + e0, scales_work[r] + b0, cs);
+            if (e == hipSuccess && nranks > 1)
+                e = qar::launch_quantize_reduce(xin(last), kind, (int)last, rp, (int)nranks, cn, (int)block,
+                                                codes_work[last] + e0, scales_work[last] + b0, codes_work[0] + e0,
+                                                scales_work[0] + b0, oc, okind, cs);
+            else if (e == hipSuccess)
+                e = qar::launch_reduce(rp, 1, cn, (int)block, codes_work[0] + e0, scales_work[0] + b0, oc, okind, cs);
         } else {
             const uint32_t s0 = (uint32_t)(c % nranks);
             int8_t* const q = codes_work[0] + e0;

@@ -204,7 +204,9 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
  *   QAR_SCHEDULE_ONE_SHOT: every rank's chunk is quantized
  *     (codes_work[r], scales_work[r]), then one fused reduce in rank order
  *     0..N-1 requantizes the sum in place into codes_work[0]/scales_work[0]
- *     and writes its dequantized value to out.
+ *     and writes its dequantized value to out.  The last rank's quantize
+ *     runs inside that reduce (qar_quantize_reduce) when N > 1; the results
+ *     are the same bits.
  *   QAR_SCHEDULE_RING: chunk c starts at rank s = c mod N, as the chunk
  *     rank s injects first in a ring: quantize(x_s), then ring steps adding
  *     x_{s+1}, ..., x_{s+N-1} (ranks mod N) in place in codes_work[0] /

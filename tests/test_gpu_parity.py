@@ -290,7 +290,7 @@ def _oracle_allreduce(o, xs, block, schedule, nchunks):
 
 @pytest.mark.parametrize("schedule", ["one_shot", "ring"])
 @pytest.mark.parametrize("nranks,nchunks,nstreams,dtype,block", [
-    (2, 1, 1, "bf16", 256), (3, 3, 2, "bf16", 128), (4, 4, 4, "bf16", 256), (4, 16, 4, "f32", 64),
+    (1, 2, 2, "bf16", 128), (2, 1, 1, "bf16", 256), (3, 3, 2, "bf16", 128), (4, 4, 4, "bf16", 256), (4, 16, 4, "f32", 64),
     (8, 8, 4, "bf16", 256), (5, 7, 3, "f32", 128)])
 def test_allreduce_simulated(oracle_lib, schedule, nranks, nchunks, nstreams, dtype, block):
     n = ragged_n(block, tiles=3)
