@@ -334,3 +334,31 @@ def test_e4m3_beyond_2_pow_31_elements(oracle_lib):
     assert_same_f32(to_host(fs[pk]), ws, "step scales")
     del x0, x1, c0, c1, s0, s1, y1, fc, fs
     torch.cuda.empty_cache()
+
+
+def test_golden_e4m3_cases_on_gpu():
+    """The hand-derived E4M3 cases through the C ABI."""
+    import golden_cases as gc
+    g = gc.load_e4m3()
+    B = g["block"]
+    for case in g["quantize"]:
+        say(f"e4m3 golden: {case['name']}")
+        codes, scales = qar.qar_quantize_blocks_e4m3(to_dev(gc.e4m3_x(case, B)), B)
+        y = qar.qar_dequantize_e4m3(codes, scales, B, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        want = gc.e4m3_bytes(case["codes"])
+        assert list(_codes(codes)[:len(want)]) == want, case["name"]
+        assert to_host(scales).view(np.uint32)[0] == np.float32(gc.e4m3_scale(case)).view(np.uint32), case["name"]
+        assert list(to_host(y).view(np.uint32)[:len(want)]) == gc.e4m3_dequant_bits(case), case["name"]
+    for case in g["reduce"]:
+        q = [qar.qar_quantize_blocks_e4m3(to_dev(gc.pad(r, B)), B) for r in case["ranks"]]
+        oc, os_ = qar.qar_reduce_quantized_e4m3([c for c, _ in q], [s for _, s in q], B)
+        torch.cuda.synchronize()
+        assert list(_codes(oc)[:len(case["codes"])]) == gc.e4m3_bytes(case["codes"]), case["name"]
+        assert to_host(os_)[0] == np.float32(case["scale"]), case["name"]
+    for case in g["ring_step"]:
+        c = to_dev(gc.pad(gc.e4m3_bytes(case["codes_in"]), B, np.uint8))
+        oc, os_ = qar.qar_ring_step_e4m3(c, to_dev(np.float32([case["scale_in"]])), to_dev(gc.pad(case["local"], B)), B)
+        torch.cuda.synchronize()
+        assert list(_codes(oc)[:len(case["codes"])]) == gc.e4m3_bytes(case["codes"]), case["name"]
+        assert to_host(os_)[0] == np.float32(case["scale"]), case["name"]
