@@ -1,0 +1,99 @@
+"""Seeded random configurations through every flat call, int8 and E4M3
+codes, against the oracle bit for bit: rank count, block size, input type,
+output type, size (whole blocks, from one block to several tiles) and the
+value distribution all drawn per case."""
+import numpy as np
+import pytest
+import torch
+
+from block_wise_int8_amd import qar, synth
+from gpu_util import assert_same_bits16, assert_same_codes, assert_same_f32, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+CASES = 40
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qar.lib()
+
+
+def _draw(rng, n, block, dtype):
+    kind = rng.integers(0, 4)
+    if kind == 0:
+        v = rng.normal(0, 1, n)
+    elif kind == 1:
+        v = rng.laplace(0, 0.5, n) * np.repeat(np.exp(rng.normal(0, 3, n // block)), block)
+    elif kind == 2:
+        v = rng.normal(0, 1, n)
+        v[rng.integers(0, n, max(1, n // 500))] *= 1000.0
+    else:
+        v = rng.integers(-3, 4, n).astype(np.float64) * 0.5          # ties and zeros
+    v = v.astype(np.float32)
+    return synth.f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+def _same_out(got, want, dtype, what):
+    if dtype == "bf16":
+        assert_same_bits16(got, want, what)
+    else:
+        assert_same_f32(got, want, what)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_configuration(oracle_lib, case):
+    rng = np.random.default_rng(10_000 + case)
+    block = int(rng.choice([64, 128, 256]))
+    nranks = int(rng.integers(1, 12))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    n = int(rng.integers(1, 3 * 4096 // block + 3)) * block
+    codes_fmt = str(rng.choice(["int8", "e4m3"]))
+    own = int(rng.integers(0, nranks))
+    say(f"random case {case}: {codes_fmt} N={nranks} own={own} B={block} n={n} {dtype}")
+    if codes_fmt == "int8":
+        quant, red, qred, ring, deq = (qar.qar_quantize_blocks, qar.qar_reduce_quantized, qar.qar_quantize_reduce,
+                                       qar.qar_ring_step, qar.qar_dequantize)
+        o_quant, o_red, o_ring, o_deq = (oracle_lib.quantize, oracle_lib.reduce, oracle_lib.ring_step,
+                                         oracle_lib.dequantize)
+        view = lambda t: to_host(t)
+    else:
+        quant, red, qred, ring, deq = (qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3,
+                                       qar.qar_quantize_reduce_e4m3, qar.qar_ring_step_e4m3, qar.qar_dequantize_e4m3)
+        o_quant, o_red, o_ring, o_deq = (oracle_lib.quantize_e4m3, oracle_lib.reduce_e4m3,
+                                         oracle_lib.ring_step_e4m3, oracle_lib.dequantize_e4m3)
+        view = lambda t: to_host(t).view(np.uint8)
+    xs = [_draw(rng, n, block, dtype) for _ in range(nranks)]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    # quantize every rank
+    q = [quant(to_dev(x), block) for x in xs]
+    wq = [o_quant(x, block) for x in xs]
+    # reduce with an output of the input type
+    out = torch.empty(n, dtype=tdt, device="cuda:0")
+    rc, rs = red([c for c, _ in q], [s for _, s in q], block, out=out)
+    # the one-kernel step with rank own quantized inside
+    own_c, own_s = torch.empty_like(q[own][0]), torch.empty_like(q[own][1])
+    qc = [c for c, _ in q]
+    qs = [s for _, s in q]
+    qc[own], qs[own] = own_c, own_s
+    fc, fs = qred(to_dev(xs[own]), own, qc, qs, block)
+    # a ring step from rank 0 with rank N-1's data, and a dequantize
+    gc_, gs_ = ring(q[0][0], q[0][1], to_dev(xs[-1]), block)
+    y = deq(rc, rs, block, out_dtype=tdt)
+    torch.cuda.synchronize()
+    for r, ((c, s), (wc, ws)) in enumerate(zip(q, wq)):
+        assert_same_codes(view(c), wc, f"rank {r} codes")
+        assert_same_f32(to_host(s), ws, f"rank {r} scales")
+    wc, ws = o_red([a for a, _ in wq], [b for _, b in wq], block)
+    assert_same_codes(view(rc), wc, "reduce codes")
+    assert_same_f32(to_host(rs), ws, "reduce scales")
+    _same_out(to_host(out), o_deq(wc, ws, block, dtype), dtype, "fused out")
+    _same_out(to_host(y), o_deq(wc, ws, block, dtype), dtype, "dequantize")
+    assert_same_codes(view(own_c), wq[own][0], "own codes")
+    assert_same_codes(view(fc), wc, "one-kernel step codes")
+    assert_same_f32(to_host(fs), ws, "one-kernel step scales")
+    rgc, rgs = o_ring(wq[0][0], wq[0][1], xs[-1], block)
+    assert_same_codes(view(gc_), rgc, "ring codes")
+    assert_same_f32(to_host(gs_), rgs, "ring scales")
