@@ -1,7 +1,7 @@
 // qar_device.h -- device-side building blocks of libqar's gfx950 kernels.
 //
 // Work decomposition shared by every kernel: a lane owns 16 consecutive
-// elements (one 16-byte vector of int8 codes), a 256-thread workgroup owns a
+// elements (one 16-byte vector of one-byte codes), a 256-thread workgroup owns a
 // tile of 4096 elements, and a block of B elements is B/16 adjacent lanes
 // (4, 8 or 16) inside one DPP row of a wavefront.  Blocks never straddle
 // lanes, wavefronts or tiles, so a block's absmax is a reduction over its

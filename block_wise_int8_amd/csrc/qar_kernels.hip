@@ -4,8 +4,10 @@
 // Distributed Machine Learning Acceleration"), page summary, section
 // "technical framework": blocks (step 1), dynamic per-block quantization to
 // INT8 (step 2, with the run-time range of "key design" item 1), reduction of
-// quantized contributions (step 3), dequantization (step 4).  The arithmetic
-// each kernel performs is spelled out in include/qar.h.
+// quantized contributions (step 3), dequantization (step 4).  The flat kernels
+// take the code format as a policy (Int8Codes, or E4M3Codes for the FP8
+// variant of the TACO page, "Why FP8?"); both are one byte per element.  The
+// arithmetic each kernel performs is spelled out in include/qar.h.
 //
 // Every kernel streams HBM once: 16-byte loads and stores per lane, a block's
 // absmax by DPP inside its lanes, the requantization fused behind the
