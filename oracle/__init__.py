@@ -63,10 +63,15 @@ class Oracle:
         lib.oracle_e4m3_encode.restype = None
         lib.oracle_e4m3_decode.argtypes = [vp, sz, vp]
         lib.oracle_e4m3_decode.restype = None
+        lib.oracle_quantize_int4.argtypes = [vp, ctypes.c_int, sz, sz, vp, vp]
+        lib.oracle_dequantize_int4.argtypes = [vp, vp, sz, sz, ctypes.c_int, vp]
+        lib.oracle_reduce_int4.argtypes = [vp, vp, sz, sz, sz, vp, vp]
+        lib.oracle_ring_step_int4.argtypes = [vp, vp, vp, ctypes.c_int, sz, sz, vp, vp]
         for name in ("oracle_quantize", "oracle_dequantize_f32", "oracle_dequantize_bf16",
                      "oracle_reduce", "oracle_ring_step", "oracle_reduce_unquantized",
                      "oracle_quantize_e4m3", "oracle_dequantize_e4m3", "oracle_reduce_e4m3",
-                     "oracle_ring_step_e4m3"):
+                     "oracle_ring_step_e4m3", "oracle_quantize_int4", "oracle_dequantize_int4",
+                     "oracle_reduce_int4", "oracle_ring_step_int4"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
 
@@ -261,6 +266,68 @@ class Oracle:
         out = np.empty(c.size, np.float32)
         self.lib.oracle_e4m3_decode(self._ptr(c), c.size, self._ptr(out))
         return out
+
+    # -- 4-bit integer codes, two per byte --------------------------------
+    @staticmethod
+    def int4_bytes(n: int) -> int:
+        return (n + 1) // 2
+
+    def quantize_int4(self, x: np.ndarray, block: int):
+        """x -> (packed codes uint8[ceil(n/2)], scales float32[nb])."""
+        x = np.ascontiguousarray(x).reshape(-1)
+        n = x.size
+        codes = np.zeros(self.int4_bytes(n), np.uint8)
+        scales = np.empty(self.nblocks(n, block), np.float32)
+        rc = self.lib.oracle_quantize_int4(self._ptr(x), self._dtype_of(x), n, block, self._ptr(codes),
+                                           self._ptr(scales))
+        self._check(rc, "quantize_int4")
+        return codes, scales
+
+    def dequantize_int4(self, codes: np.ndarray, scales: np.ndarray, block: int, n: int, out: str = "f32"):
+        codes = np.ascontiguousarray(codes, np.uint8).reshape(-1)
+        scales = np.ascontiguousarray(scales, np.float32).reshape(-1)
+        if codes.size < self.int4_bytes(n) or scales.size < self.nblocks(n, block):
+            raise ValueError("too few codes or scales")
+        if out not in ("f32", "bf16"):
+            raise ValueError(out)
+        res = np.empty(n, np.float32 if out == "f32" else np.uint16)
+        rc = self.lib.oracle_dequantize_int4(self._ptr(codes), self._ptr(scales), n, block,
+                                             F32 if out == "f32" else BF16, self._ptr(res))
+        self._check(rc, "dequantize_int4")
+        return res
+
+    def reduce_int4(self, codes: list, scales: list, block: int, n: int):
+        nranks = len(codes)
+        if nranks == 0 or nranks != len(scales):
+            raise ValueError("need one scales array per codes array, at least one rank")
+        codes = [np.ascontiguousarray(c, np.uint8).reshape(-1) for c in codes]
+        scales = [np.ascontiguousarray(s, np.float32).reshape(-1) for s in scales]
+        nb = self.nblocks(n, block)
+        for c, s in zip(codes, scales):
+            if c.size < self.int4_bytes(n) or s.size < nb:
+                raise ValueError("rank buffers too small")
+        cptr = (ctypes.c_void_p * nranks)(*[self._ptr(c) for c in codes])
+        sptr = (ctypes.c_void_p * nranks)(*[self._ptr(s) for s in scales])
+        out_c = np.zeros(self.int4_bytes(n), np.uint8)
+        out_s = np.empty(nb, np.float32)
+        rc = self.lib.oracle_reduce_int4(ctypes.cast(cptr, ctypes.c_void_p), ctypes.cast(sptr, ctypes.c_void_p),
+                                         nranks, n, block, self._ptr(out_c), self._ptr(out_s))
+        self._check(rc, "reduce_int4")
+        return out_c, out_s
+
+    def ring_step_int4(self, codes_in: np.ndarray, scales_in: np.ndarray, local: np.ndarray, block: int):
+        local = np.ascontiguousarray(local).reshape(-1)
+        n = local.size
+        codes_in = np.ascontiguousarray(codes_in, np.uint8).reshape(-1)
+        scales_in = np.ascontiguousarray(scales_in, np.float32).reshape(-1)
+        if codes_in.size < self.int4_bytes(n) or scales_in.size < self.nblocks(n, block):
+            raise ValueError("size mismatch")
+        out_c = np.zeros(self.int4_bytes(n), np.uint8)
+        out_s = np.empty(self.nblocks(n, block), np.float32)
+        rc = self.lib.oracle_ring_step_int4(self._ptr(codes_in), self._ptr(scales_in), self._ptr(local),
+                                            self._dtype_of(local), n, block, self._ptr(out_c), self._ptr(out_s))
+        self._check(rc, "ring_step_int4")
+        return out_c, out_s
 
 
 _default = None

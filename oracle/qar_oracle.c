@@ -496,3 +496,163 @@ void oracle_e4m3_decode(const uint8_t* in, size_t n, float* out)
     for (size_t i = 0; i < n; i++)
         out[i] = e4m3_value(in[i]);
 }
+
+/* ------------------------------------------------------------------------
+ * 4-bit integer codes.  The pages name 4-bit communication quantization only
+ * through the titles of later work in their reference lists ("SDP4Bit:
+ * Toward 4-bit Communication Quantization in Sharded Data Parallelism ...",
+ * "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication ..."); no
+ * format is described.  The reading here is the int8 method at 4 bits:
+ *   scale  s   = fl32(absmax / 7)
+ *   code   q_i = 0 if s == 0, else clamp(rne(fl32(x_i / s)), -7, 7)
+ *   value  y_i = fl32((float)q_i * s)
+ *   reduce and ring: as for int8 codes, with this quantizer and value.
+ * Storage: two codes per byte, two's complement nibbles, element 2k in the
+ * low nibble of byte k and element 2k+1 in the high nibble (by element index,
+ * whatever the block length); a buffer of n elements takes ceil(n/2) bytes.
+ * ------------------------------------------------------------------------ */
+
+static int nibble_get(const uint8_t* p, size_t i)
+{
+    unsigned v = (p[i / 2] >> (4 * (i % 2))) & 0xFu;
+    return v >= 8 ? (int)v - 16 : (int)v;
+}
+
+static void nibble_set(uint8_t* p, size_t i, int q)
+{
+    unsigned shift = 4 * (unsigned)(i % 2);
+    p[i / 2] = (uint8_t)((p[i / 2] & ~(0xFu << shift)) | (((unsigned)q & 0xFu) << shift));
+}
+
+/* codes of one block starting at element `start` of the packed buffer */
+static void quantize_one_block_int4(const float* v, size_t len, uint8_t* packed, size_t start, float* scale)
+{
+    float absmax = 0.0f;
+    for (size_t i = 0; i < len; i++) {
+        float m = fabsf(v[i]);
+        if (m > absmax)
+            absmax = m;
+    }
+    float s = absmax / 7.0f;
+    *scale = s;
+    for (size_t i = 0; i < len; i++) {
+        if (s == 0.0f) {
+            nibble_set(packed, start + i, 0);
+            continue;
+        }
+        float t = v[i] / s;
+        float r = nearbyintf(t); /* to nearest, ties to even */
+        if (r > 7.0f)
+            r = 7.0f;
+        if (r < -7.0f)
+            r = -7.0f;
+        nibble_set(packed, start + i, (int)r);
+    }
+}
+
+static float dequant_value_int4(const uint8_t* packed, size_t i, float s)
+{
+    return (float)nibble_get(packed, i) * s;
+}
+
+int oracle_quantize_int4(const void* x, int dtype, size_t n, size_t block, uint8_t* codes, float* scales)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    if (!x || !codes || !scales)
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(x, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* v = malloc(block * sizeof *v);
+    if (!v)
+        return ORACLE_BAD_ARG;
+    memset(codes, 0, (n + 1) / 2);
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            v[i] = load_element(x, dtype, start + i);
+        quantize_one_block_int4(v, len, codes, start, scales + b);
+    }
+    free(v);
+    return ORACLE_OK;
+}
+
+int oracle_dequantize_int4(const uint8_t* codes, const float* scales, size_t n, size_t block,
+                           int out_dtype, void* out)
+{
+    if (block == 0 || (out_dtype != ORACLE_BF16 && out_dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    for (size_t i = 0; i < n; i++) {
+        float y = dequant_value_int4(codes, i, scales[i / block]);
+        if (out_dtype == ORACLE_BF16)
+            ((uint16_t*)out)[i] = float_to_bf16_bits(y);
+        else
+            ((float*)out)[i] = y;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_reduce_int4(const uint8_t* const* codes, const float* const* scales, size_t nranks, size_t n,
+                       size_t block, uint8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || nranks == 0)
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    memset(codes_out, 0, (n + 1) / 2);
+    size_t nb = block_count(n, block);
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value_int4(codes[0], start + i, scales[0][b]);
+        for (size_t r = 1; r < nranks; r++)
+            for (size_t i = 0; i < len; i++)
+                acc[i] = acc[i] + dequant_value_int4(codes[r], start + i, scales[r][b]);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
+        quantize_one_block_int4(acc, len, codes_out, start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}
+
+int oracle_ring_step_int4(const uint8_t* codes_in, const float* scales_in, const void* local, int dtype,
+                          size_t n, size_t block, uint8_t* codes_out, float* scales_out)
+{
+    if (block == 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_F32))
+        return ORACLE_BAD_ARG;
+    if (n == 0)
+        return ORACLE_OK;
+    for (size_t i = 0; i < n; i++)
+        if (!isfinite(load_element(local, dtype, i)))
+            return ORACLE_NONFINITE;
+    float* acc = malloc(block * sizeof *acc);
+    if (!acc)
+        return ORACLE_BAD_ARG;
+    size_t nb = block_count(n, block);
+    /* codes_out may not alias codes_in here: the nibbles are rewritten */
+    for (size_t b = 0; b < nb; b++) {
+        size_t start = b * block;
+        size_t len = (n - start < block) ? n - start : block;
+        for (size_t i = 0; i < len; i++)
+            acc[i] = dequant_value_int4(codes_in, start + i, scales_in[b]) + load_element(local, dtype, start + i);
+        if (!all_finite(acc, len)) {
+            free(acc);
+            return ORACLE_NONFINITE;
+        }
+        quantize_one_block_int4(acc, len, codes_out, start, scales_out + b);
+    }
+    free(acc);
+    return ORACLE_OK;
+}

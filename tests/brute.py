@@ -244,3 +244,42 @@ def ring_step_e4m3(codes: list[int], scales: list[Fraction], local: list[Fractio
     neg = [v == 0 and a == 0 and b == 0 and na and nb
            for v, a, b, na, nb in zip(acc, y, local, ny, local_neg_zero)]
     return quantize_e4m3(acc, block, neg)
+
+
+# ---------------------------------------------------------------------------
+# 4-bit integer codes: the int8 rules with 7 in place of 127 (codes -7..7).
+
+CODES4 = range(-7, 8)
+
+
+def nearest_code4(t: Fraction) -> int:
+    best = None
+    for q in CODES4:
+        d = abs(t - q)
+        if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+            best = (d, q)
+    return best[1]
+
+
+def quantize4(values: list[Fraction], block: int) -> tuple[list[int], list[Fraction]]:
+    """-> (codes -7..7 per element, scales); packing is the caller's."""
+    codes, scales = [], []
+    for start in range(0, len(values), block):
+        blk = values[start:start + block]
+        absmax = max((abs(v) for v in blk), default=Fraction(0))
+        s = rn32(absmax / 7)
+        codes += [0] * len(blk) if s == 0 else [nearest_code4(rn32(v / s)) for v in blk]
+        scales.append(s)
+    return codes, scales
+
+
+def reduce4(rank_codes: list[list[int]], rank_scales: list[list[Fraction]], block: int):
+    acc = [rn32(q * rank_scales[0][i // block]) for i, q in enumerate(rank_codes[0])]
+    for c, s in zip(rank_codes[1:], rank_scales[1:]):
+        acc = [rn32(a + rn32(q * s[i // block])) for i, (a, q) in enumerate(zip(acc, c))]
+    return quantize4(acc, block)
+
+
+def ring_step4(codes: list[int], scales: list[Fraction], local: list[Fraction], block: int):
+    acc = [rn32(rn32(q * scales[i // block]) + x) for i, (q, x) in enumerate(zip(codes, local))]
+    return quantize4(acc, block)

@@ -9,13 +9,14 @@ import pytest
 import oracle
 import pins
 import pins_e4m3
+import pins_int4
 
 MUTANTS = {
-    "round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
+    "round_half_away": ("float r = nearbyintf(t); /* default rounding mode", "float r = roundf(t); /* default rounding mode"),
     "scale_over_128": ("float s = absmax / 127.0f;", "float s = absmax / 128.0f;"),
     "scale_by_reciprocal": ("float s = absmax / 127.0f;", "float s = absmax * (1.0f / 127.0f);"),
-    "quotient_by_reciprocal": ("float t = v[i] / s;\n        float r = nearbyintf(t);",
-                               "float t = v[i] * (1.0f / s);\n        float r = nearbyintf(t);"),
+    "quotient_by_reciprocal": ("float t = v[i] / s;\n        float r = nearbyintf(t); /* default",
+                               "float t = v[i] * (1.0f / s);\n        float r = nearbyintf(t); /* default"),
     "clamp_to_minus_128": ("if (r < -127.0f)\n            r = -127.0f;",
                            "if (r < -128.0f)\n            r = -128.0f;"),
     "no_clamp": ("if (r > 127.0f)\n            r = 127.0f;\n        if (r < -127.0f)\n            r = -127.0f;\n",
@@ -58,8 +59,19 @@ MUTANTS = {
                         "acc[i] = fmaf(e4m3_value(codes[r][start + i]), scales[r][b], acc[i]);"),
     "e4m3_ring_subtracts": ("acc[i] = dequant_value_e4m3(codes_in[start + i], scales_in[b]) +",
                             "acc[i] = dequant_value_e4m3(codes_in[start + i], scales_in[b]) -"),
-    "e4m3_dequant_bf16_truncates": ("((uint16_t*)out)[i] = float_to_bf16_bits(y);",
-                                    "{ uint32_t u_; memcpy(&u_, &y, 4); ((uint16_t*)out)[i] = (uint16_t)(u_ >> 16); }"),
+    "e4m3_dequant_bf16_truncates": ("dequant_value_e4m3(codes[i], scales[i / block]);\n        if (out_dtype == ORACLE_BF16)\n            ((uint16_t*)out)[i] = float_to_bf16_bits(y);",
+                                    "dequant_value_e4m3(codes[i], scales[i / block]);\n        if (out_dtype == ORACLE_BF16)\n            { uint32_t u_; memcpy(&u_, &y, 4); ((uint16_t*)out)[i] = (uint16_t)(u_ >> 16); }"),
+    # 4-bit codes
+    "int4_scale_over_8": ("float s = absmax / 7.0f;", "float s = absmax / 8.0f;"),
+    "int4_ties_away": ("float r = nearbyintf(t); /* to nearest, ties to even */",
+                       "float r = roundf(t); /* to nearest, ties to even */"),
+    "int4_clamp_8": ("if (r < -7.0f)\n            r = -7.0f;", "if (r < -8.0f)\n            r = -8.0f;"),
+    "int4_nibbles_swapped": ("unsigned shift = 4 * (unsigned)(i % 2);", "unsigned shift = 4 * (unsigned)(1 - i % 2);"),
+    "int4_sign_extension": ("return v >= 8 ? (int)v - 16 : (int)v;", "return v >= 8 ? (int)v - 15 : (int)v;"),
+    "int4_reduce_order": ("acc[i] = acc[i] + dequant_value_int4(codes[r], start + i, scales[r][b]);",
+                          "acc[i] = acc[i] + dequant_value_int4(codes[nranks - r], start + i, scales[nranks - r][b]);"),
+    "int4_ring_subtracts": ("dequant_value_int4(codes_in, start + i, scales_in[b]) + load_element",
+                            "dequant_value_int4(codes_in, start + i, scales_in[b]) - load_element"),
 }
 
 
@@ -73,7 +85,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
     lib = oracle.build(str(path), str(tmp_path / f"lib{name}.so"))
     mutant = oracle.Oracle(lib)
     caught = None
-    for pin in pins.ALL_PINS + pins_e4m3.ALL_PINS:
+    for pin in pins.ALL_PINS + pins_e4m3.ALL_PINS + pins_int4.ALL_PINS:
         try:
             pin(mutant)
         except (AssertionError, ValueError) as e:

@@ -5,8 +5,9 @@ import pytest
 
 import pins
 import pins_e4m3
+import pins_int4
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + pins_e4m3.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins_e4m3.ALL_PINS + pins_int4.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(oracle_lib, pin):
     pin(oracle_lib)

@@ -102,3 +102,18 @@ def test_reduce_e4m3_any_codes(oracle_lib, nranks, block, nblocks, data):
                                [[Fraction(float(v)) for v in s] for s in scales], block)
     assert list(oc.astype(int)) == bc
     assert [Fraction(float(v)) for v in os_] == bs
+
+
+# ----------------------------------------------------------------------------
+# 4-bit codes
+
+
+@COMMON
+@given(st.lists(FINITE_F32, min_size=1, max_size=24), st.integers(1, 9))
+def test_quantize_int4_fp32_any_bits(oracle_lib, bits, block):
+    import pins_int4
+    x = _f32(bits)
+    packed, scales = oracle_lib.quantize_int4(x, block)
+    bc, bs = brute.quantize4([Fraction(float(v)) for v in x], block)
+    assert list(pins_int4.unpack(packed, x.size).astype(int)) == bc
+    assert [Fraction(float(s)) for s in scales] == bs
