@@ -51,9 +51,12 @@ qar_status check_common(size_t n, uint32_t block) {
     return QAR_OK;
 }
 
+// Bytes of n codes: one per element, or one per two elements for 4-bit codes.
+size_t code_bytes(size_t n, int code) { return code == qar::kCodeInt4 ? n / 2 : n; }
+
 qar_status check_reduce(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
                         uint32_t block, int8_t* codes_out, float* scales_out, void* out,
-                        qar_dtype out_dtype) {
+                        qar_dtype out_dtype, int code = qar::kCodeInt8) {
     qar_status st = check_common(n, block);
     if (st != QAR_OK) return st;
     if (!codes || !scales || !codes_out || !scales_out) return QAR_ERR_INVALID_ARG;
@@ -62,7 +65,8 @@ qar_status check_reduce(const int8_t* const* codes, const float* const* scales, 
     const size_t nb = n / block;
     if (!aligned(codes_out, 16) || !aligned(scales_out, 4) || (out && !aligned(out, 16)))
         return QAR_ERR_MISALIGNED;
-    const Range co = range(codes_out, n), so = range(scales_out, nb * 4);
+    const size_t cb = code_bytes(n, code);
+    const Range co = range(codes_out, cb), so = range(scales_out, nb * 4);
     if (overlap(co, so)) return QAR_ERR_INVALID_ARG;
     Range oo{0, 0};
     if (out) {
@@ -73,7 +77,7 @@ qar_status check_reduce(const int8_t* const* codes, const float* const* scales, 
     for (uint32_t r = 0; r < nranks; ++r) {
         if (!codes[r] || !scales[r]) return QAR_ERR_INVALID_ARG;
         if (!aligned(codes[r], 16) || !aligned(scales[r], 4)) return QAR_ERR_MISALIGNED;
-        const Range ci = range(codes[r], n), si = range(scales[r], nb * 4);
+        const Range ci = range(codes[r], cb), si = range(scales[r], nb * 4);
         if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci))
             return QAR_ERR_INVALID_ARG;
         if (out && (overlap(oo, ci) || overlap(oo, si))) return QAR_ERR_INVALID_ARG;
@@ -155,7 +159,7 @@ static qar_status quantize_impl(const void* x, qar_dtype dtype, size_t n, uint32
     if (!x || !codes || !scales) return QAR_ERR_INVALID_ARG;
     if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return QAR_ERR_MISALIGNED;
-    const Range xi = range(x, n * dtype_bytes(dtype)), co = range(codes, n),
+    const Range xi = range(x, n * dtype_bytes(dtype)), co = range(codes, code_bytes(n, code)),
                 so = range(scales, n / block * 4);
     if (overlap(xi, co) || overlap(xi, so) || overlap(co, so)) return QAR_ERR_INVALID_ARG;
     const hipError_t e = qar::launch_quantize(x, dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32, n,
@@ -174,11 +178,17 @@ qar_status qar_quantize_blocks_e4m3(const void* x, qar_dtype dtype, size_t n, ui
                          "qar_quantize_blocks_e4m3");
 }
 
+qar_status qar_quantize_blocks_int4(const void* x, qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes,
+                                    float* scales, void* stream) {
+    return quantize_impl(x, dtype, n, block, (int8_t*)codes, scales, stream, qar::kCodeInt4,
+                         "qar_quantize_blocks_int4");
+}
+
 static qar_status reduce_impl(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
                               uint32_t block, int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
                               void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
-    qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
+    qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype, code);
     if (st != QAR_OK) return st;
     qar::RankPtrs rp;
     fill_ranks(rp, codes, scales, nranks, 0, 0);
@@ -201,6 +211,13 @@ qar_status qar_reduce_quantized_e4m3(const uint8_t* const* codes, const float* c
                        out_dtype, stream, qar::kCodeE4M3, "qar_reduce_quantized_e4m3");
 }
 
+qar_status qar_reduce_quantized_int4(const uint8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t n, uint32_t block, uint8_t* codes_out, float* scales_out, void* out,
+                                     qar_dtype out_dtype, void* stream) {
+    return reduce_impl((const int8_t* const*)codes, scales, nranks, n, block, (int8_t*)codes_out, scales_out, out,
+                       out_dtype, stream, qar::kCodeInt4, "qar_reduce_quantized_int4");
+}
+
 static qar_status quantize_reduce_impl(const void* x_own, qar_dtype dtype, uint32_t own, int8_t* const* codes,
                                        float* const* scales, uint32_t nranks, size_t n, uint32_t block,
                                        int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
@@ -210,13 +227,14 @@ static qar_status quantize_reduce_impl(const void* x_own, qar_dtype dtype, uint3
     if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
     if (nranks == 0 || nranks > QAR_MAX_RANKS || own >= nranks) return QAR_ERR_INVALID_ARG;
     qar_status st = check_reduce((const int8_t* const*)codes, (const float* const*)scales, nranks, n, block,
-                                 codes_out, scales_out, out, out_dtype);
+                                 codes_out, scales_out, out, out_dtype, code);
     if (st != QAR_OK) return st;
     if (!aligned(x_own, 16)) return QAR_ERR_MISALIGNED;
     const size_t nb = n / block;
     // Written: rank own's codes and scales, the result (codes, scales, out).
     // Each may overlap nothing else the call reads or writes.
-    Range w[5] = {range(codes[own], n), range(scales[own], nb * 4), range(codes_out, n),
+    const size_t cb = code_bytes(n, code);
+    Range w[5] = {range(codes[own], cb), range(scales[own], nb * 4), range(codes_out, cb),
                   range(scales_out, nb * 4), out ? range(out, n * dtype_bytes(out_dtype)) : Range{0, 0}};
     const Range xi = range(x_own, n * dtype_bytes(dtype));
     for (int i = 0; i < 5; ++i)
@@ -227,7 +245,7 @@ static qar_status quantize_reduce_impl(const void* x_own, qar_dtype dtype, uint3
             if (overlap(w[i], w[j])) return QAR_ERR_INVALID_ARG;
         for (uint32_t r = 0; r < nranks; ++r) {
             if (r == own) continue;
-            if (overlap(w[i], range(codes[r], n)) || overlap(w[i], range(scales[r], nb * 4)))
+            if (overlap(w[i], range(codes[r], cb)) || overlap(w[i], range(scales[r], nb * 4)))
                 return QAR_ERR_INVALID_ARG;
         }
     }
@@ -254,6 +272,15 @@ qar_status qar_quantize_reduce_e4m3(const void* x_own, qar_dtype dtype, uint32_t
     return quantize_reduce_impl(x_own, dtype, own, (int8_t* const*)codes, scales, nranks, n, block,
                                 (int8_t*)codes_out, scales_out, out, out_dtype, stream, qar::kCodeE4M3,
                                 "qar_quantize_reduce_e4m3");
+}
+
+qar_status qar_quantize_reduce_int4(const void* x_own, qar_dtype dtype, uint32_t own, uint8_t* const* codes,
+                                    float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                                    uint8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                                    void* stream) {
+    return quantize_reduce_impl(x_own, dtype, own, (int8_t* const*)codes, scales, nranks, n, block,
+                                (int8_t*)codes_out, scales_out, out, out_dtype, stream, qar::kCodeInt4,
+                                "qar_quantize_reduce_int4");
 }
 
 qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
@@ -312,8 +339,9 @@ static qar_status ring_step_impl(const int8_t* codes_in, const float* scales_in,
         !aligned(scales_out, 4))
         return QAR_ERR_MISALIGNED;
     const size_t nb = n / block;
-    const Range ci = range(codes_in, n), si = range(scales_in, nb * 4), li = range(local, n * dtype_bytes(dtype)),
-                co = range(codes_out, n), so = range(scales_out, nb * 4);
+    const size_t cb = code_bytes(n, code);
+    const Range ci = range(codes_in, cb), si = range(scales_in, nb * 4), li = range(local, n * dtype_bytes(dtype)),
+                co = range(codes_out, cb), so = range(scales_out, nb * 4);
     if (bad_overlap(co, ci, true) || bad_overlap(so, si, true) || overlap(co, si) || overlap(so, ci) ||
         overlap(co, li) || overlap(so, li) || overlap(co, so))
         return QAR_ERR_INVALID_ARG;
@@ -337,6 +365,13 @@ qar_status qar_ring_step_e4m3(const uint8_t* codes_in, const float* scales_in, c
                           scales_out, stream, qar::kCodeE4M3, "qar_ring_step_e4m3");
 }
 
+qar_status qar_ring_step_int4(const uint8_t* codes_in, const float* scales_in, const void* local,
+                              qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes_out, float* scales_out,
+                              void* stream) {
+    return ring_step_impl((const int8_t*)codes_in, scales_in, local, dtype, n, block, (int8_t*)codes_out,
+                          scales_out, stream, qar::kCodeInt4, "qar_ring_step_int4");
+}
+
 static qar_status dequantize_impl(const int8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
                                   qar_dtype out_dtype, void* stream, int code, const char* name) {
     if (n == 0) return QAR_OK;
@@ -345,7 +380,7 @@ static qar_status dequantize_impl(const int8_t* codes, const float* scales, size
     if (!codes || !scales || !out) return QAR_ERR_INVALID_ARG;
     if (!dtype_ok(out_dtype)) return QAR_ERR_UNSUPPORTED;
     if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16)) return QAR_ERR_MISALIGNED;
-    const Range ci = range(codes, n), si = range(scales, n / block * 4),
+    const Range ci = range(codes, code_bytes(n, code)), si = range(scales, n / block * 4),
                 oo = range(out, n * dtype_bytes(out_dtype));
     if (overlap(oo, ci) || overlap(oo, si)) return QAR_ERR_INVALID_ARG;
     const hipError_t e = qar::launch_dequantize(codes, scales, n, (int)block, out, out_kind(out, out_dtype),
@@ -362,6 +397,12 @@ qar_status qar_dequantize_e4m3(const uint8_t* codes, const float* scales, size_t
                                qar_dtype out_dtype, void* stream) {
     return dequantize_impl((const int8_t*)codes, scales, n, block, out, out_dtype, stream, qar::kCodeE4M3,
                            "qar_dequantize_e4m3");
+}
+
+qar_status qar_dequantize_int4(const uint8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                               qar_dtype out_dtype, void* stream) {
+    return dequantize_impl((const int8_t*)codes, scales, n, block, out, out_dtype, stream, qar::kCodeInt4,
+                           "qar_dequantize_int4");
 }
 
 qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t n, qar_dtype dtype, void* out,

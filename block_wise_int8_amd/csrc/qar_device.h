@@ -36,6 +36,18 @@ __device__ __forceinline__ void store_b128(void* p, uint4 q) {
     __builtin_nontemporal_store(v, reinterpret_cast<qar_u32x4*>(p));
 }
 
+typedef unsigned int qar_u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_b64(const void* p) {
+    const qar_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const qar_u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ void store_b64(void* p, uint2 q) {
+    const qar_u32x2 v = {q.x, q.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<qar_u32x2*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // tile order across the chip's eight XCDs
 //
@@ -181,19 +193,40 @@ __device__ __forceinline__ void dequantize16(uint4 q, float s, float (&y)[kLaneE
 }
 
 // ---------------------------------------------------------------------------
-// code formats.  Both are one byte per element, so every kernel's layout and
-// traffic is the same; the format decides Q_max (the value a block's absmax
-// maps to), how a quotient becomes a byte and what a byte is worth.
+// code formats.  A policy gives Q_max (the value a block's absmax maps to),
+// the type of a lane's 16 codes (Vec) and how to load, store, make and read
+// them.  Byte-wide formats (int8, E4M3) keep a lane's codes in one 16-byte
+// vector at byte offset e0; the 4-bit format packs them into 8 bytes at e0/2.
+// slot8/slot4 read the codes of 8 or 4 consecutive elements starting at e
+// (a multiple of 8 or 4) from global memory or LDS, for the kernels that
+// write their output in contiguous 16-byte slots.
 
 // EQuARX's integers: q = clamp(rne(x/s), -127, 127), s = absmax / 127.
 struct Int8Codes {
+    using Vec = uint4;
     static constexpr float kQmax = 127.0f;
+    static __device__ __forceinline__ size_t bytes(size_t e) { return e; }
+    static __device__ __forceinline__ Vec load(const int8_t* c, size_t e0) { return load_b128(c + e0); }
+    static __device__ __forceinline__ void store(int8_t* c, size_t e0, Vec q) { store_b128(c + e0, q); }
     static __device__ __forceinline__ float value(uint32_t w, int k) { return code_f32(w, k); }
-    static __device__ __forceinline__ uint4 quantize(const float (&v)[kLaneElems], float s) {
+    static __device__ __forceinline__ Vec quantize(const float (&v)[kLaneElems], float s) {
         return quantize16(v, s);
     }
-    static __device__ __forceinline__ void dequantize(uint4 q, float s, float (&y)[kLaneElems]) {
+    static __device__ __forceinline__ void dequantize(Vec q, float s, float (&y)[kLaneElems]) {
         dequantize16(q, s, y);
+    }
+    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+        const uint2 w = *reinterpret_cast<const uint2*>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = value(w.x, k);
+            v[4 + k] = value(w.y, k);
+        }
+    }
+    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
     }
 };
 
@@ -210,7 +243,11 @@ struct Int8Codes {
 // exact, when s >= 2^-90.  The FMA correction keeps a nonzero quotient's
 // sign; only x = -0 needs its sign restored.
 struct E4M3Codes {
+    using Vec = uint4;
     static constexpr float kQmax = 448.0f;
+    static __device__ __forceinline__ size_t bytes(size_t e) { return e; }
+    static __device__ __forceinline__ Vec load(const int8_t* c, size_t e0) { return load_b128(c + e0); }
+    static __device__ __forceinline__ void store(int8_t* c, size_t e0, Vec q) { store_b128(c + e0, q); }
     static constexpr float kFastMinScale = 0x1p-90f;
     static __device__ __forceinline__ float value(uint32_t w, int k) {
         switch (k) {
@@ -259,6 +296,79 @@ struct E4M3Codes {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[4 * j + k] = value(w[j], k) * s;
+    }
+    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+        const uint2 w = *reinterpret_cast<const uint2*>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = value(w.x, k);
+            v[4 + k] = value(w.y, k);
+        }
+    }
+    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
+    }
+};
+
+// 4-bit integers, the int8 rules at 4 bits: q = clamp(rne(x/s), -7, 7),
+// s = absmax / 7, two codes per byte (element 2k in the low nibble of byte
+// k).  The quotient and the rounding are the int8 ones (quotients below 1/4
+// give code 0 either way); the low nibble of the rounded word is the code in
+// two's complement.
+struct Int4Codes {
+    using Vec = uint2;
+    static constexpr float kQmax = 7.0f;
+    static __device__ __forceinline__ size_t bytes(size_t e) { return e / 2; }
+    static __device__ __forceinline__ Vec load(const int8_t* c, size_t e0) { return load_b64(c + e0 / 2); }
+    static __device__ __forceinline__ void store(int8_t* c, size_t e0, Vec q) { store_b64(c + e0 / 2, q); }
+    // code k (0..7) of a word of 8 nibbles, as float
+    static __device__ __forceinline__ float value(uint32_t w, int k) {
+        return (float)((int32_t)(w << (28 - 4 * k)) >> 28);
+    }
+    static __device__ __forceinline__ uint32_t nibbles8(const uint32_t* w) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r |= (w[k] & 0xFu) << (4 * k);
+        return r;
+    }
+    static __device__ __forceinline__ Vec quantize(const float (&v)[kLaneElems], float s) {
+        uint32_t w[kLaneElems];
+        if (s >= kFastQuotientMinScale) {
+            const float r = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i) {
+                float y = v[i] * r;
+                const float e = __builtin_fmaf(-y, s, v[i]);
+                y = __builtin_fmaf(e, r, y);
+                w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(y, -kQmax, kQmax) + kRoundMagic);
+            }
+        } else if (s != 0.0f) {
+#pragma unroll
+            for (int i = 0; i < kLaneElems; ++i)
+                w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[i] / s, -kQmax, kQmax) + kRoundMagic);
+        } else {
+            return make_uint2(0u, 0u);
+        }
+        return make_uint2(nibbles8(w), nibbles8(w + 8));
+    }
+    static __device__ __forceinline__ void dequantize(Vec q, float s, float (&y)[kLaneElems]) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            y[k] = value(q.x, k) * s;
+            y[8 + k] = value(q.y, k) * s;
+        }
+    }
+    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e / 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = value(w, k);
+    }
+    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(c + e / 2);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
     }
 };
 

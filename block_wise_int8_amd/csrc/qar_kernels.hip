@@ -96,9 +96,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
         float v[kLaneElems];
         load16(x + ld, v);
         const float s = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / C::kQmax;
-        const uint4 q = C::quantize(v, s);
+        const typename C::Vec q = C::quantize(v, s);
         if (a.valid) {
-            store_b128(codes + a.e0, q);
+            C::store(codes, a.e0, q);
             if (a.leads) scales[a.blk] = s;
         }
     }
@@ -114,8 +114,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const In* __restrict__ x,
 // reads back the 8 (bf16) or 4 (fp32) codes that belong to its store slots.
 // Only lanes of one wavefront exchange data, so a wave barrier suffices.
 template <int B, int OUT, typename C = Int8Codes>
-__device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_t e0, size_t n, void* out,
-                                                       uint4* lds_codes, float* lds_scales) {
+__device__ __forceinline__ void store_dequantized_tile(typename C::Vec qo, float so, size_t e0, size_t n, void* out,
+                                                       typename C::Vec* lds_codes, float* lds_scales) {
     constexpr int kLanesPerBlock = B / kLaneElems;
     const int lane = threadIdx.x & 63;
     lds_codes[lane] = qo;
@@ -129,26 +129,28 @@ __device__ __forceinline__ void store_dequantized_tile(uint4 qo, float so, size_
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int e = 512 * j + 8 * lane; // element within the wave tile
-            const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
+            float c[8];
+            C::slot8(codes, e, c);
             const float s = lds_scales[e / B];
             uint4 o;
-            o.x = pack_bf16x2(C::value(c.x, 0) * s, C::value(c.x, 1) * s);
-            o.y = pack_bf16x2(C::value(c.x, 2) * s, C::value(c.x, 3) * s);
-            o.z = pack_bf16x2(C::value(c.y, 0) * s, C::value(c.y, 1) * s);
-            o.w = pack_bf16x2(C::value(c.y, 2) * s, C::value(c.y, 3) * s);
+            o.x = pack_bf16x2(c[0] * s, c[1] * s);
+            o.y = pack_bf16x2(c[2] * s, c[3] * s);
+            o.z = pack_bf16x2(c[4] * s, c[5] * s);
+            o.w = pack_bf16x2(c[6] * s, c[7] * s);
             if (wave0 + e < n) store_b128(static_cast<uint16_t*>(out) + wave0 + e, o);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 256 * j + 4 * lane;
-            const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
+            float c[4];
+            C::slot4(codes, e, c);
             const float s = lds_scales[e / B];
             uint4 o;
-            o.x = __builtin_bit_cast(uint32_t, C::value(c, 0) * s);
-            o.y = __builtin_bit_cast(uint32_t, C::value(c, 1) * s);
-            o.z = __builtin_bit_cast(uint32_t, C::value(c, 2) * s);
-            o.w = __builtin_bit_cast(uint32_t, C::value(c, 3) * s);
+            o.x = __builtin_bit_cast(uint32_t, c[0] * s);
+            o.y = __builtin_bit_cast(uint32_t, c[1] * s);
+            o.z = __builtin_bit_cast(uint32_t, c[2] * s);
+            o.w = __builtin_bit_cast(uint32_t, c[3] * s);
             if (wave0 + e < n) store_b128(static_cast<float*>(out) + wave0 + e, o);
         }
     }
@@ -168,7 +170,8 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
     constexpr int G = 8; // ranks whose loads are in flight together
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
-    __shared__ uint4 lds_codes[kStaged ? kThreads : 1];
+    using Vec = typename C::Vec;
+    __shared__ Vec lds_codes[kStaged ? kThreads : 1];
     __shared__ float lds_scales[kStaged ? kThreads * kLaneElems / B : 1];
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
@@ -179,16 +182,16 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
         using OwnRaw = Raw16<std::conditional_t<kOwn, OwnIn, uint16_t>>;
         OwnRaw xr{};
         if constexpr (kOwn) xr = load_raw16(x_own + ld);
-        uint4 q_own = make_uint4(0u, 0u, 0u, 0u);
+        Vec q_own{};
         float s_own = 0.0f;
         float acc[kLaneElems];
         for (int g = 0; g < nranks; g += G) {
-            uint4 q[G];
+            Vec q[G];
             float s[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 if (g + j < nranks && !(kOwn && g + j == own)) {
-                    q[j] = load_b128(rp.codes[g + j] + ld);
+                    q[j] = C::load(rp.codes[g + j], ld);
                     s[j] = rp.scales[g + j][blk];
                 }
             }
@@ -199,7 +202,7 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
                     s_own = block_max<B>(masked_absmax<Lanes>(v, a.valid)) / C::kQmax;
                     q_own = C::quantize(v, s_own);
                     if (a.valid) {
-                        store_b128(own_codes + a.e0, q_own);
+                        C::store(own_codes, a.e0, q_own);
                         if (a.leads) own_scales[a.blk] = s_own;
                     }
                 }
@@ -228,7 +231,7 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
         }
         const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / C::kQmax;
         uint32_t w[kLaneElems];
-        uint4 qo;
+        Vec qo;
         if constexpr (OUT != kOutNone && !kStaged) {
             static_assert(std::is_same<C, Int8Codes>::value, "row-bounded output is int8 only");
             qo = quantize16(acc, so, w);
@@ -236,7 +239,7 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
             qo = C::quantize(acc, so);
         }
         if (a.valid) {
-            store_b128(codes_out + a.e0, qo);
+            C::store(codes_out, a.e0, qo);
             if (a.leads) scales_out[a.blk] = so;
         }
         if constexpr (kStaged) {
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
         const size_t blk = a.valid ? a.blk : 0;
         float acc[kLaneElems];
         {
-            const uint4 q = load_b128(codes_in + ld);
+            const typename C::Vec q = C::load(codes_in, ld);
             const float s = scales_in[blk];
             float x[kLaneElems];
             load16(local + ld, x);
@@ -299,9 +302,9 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
             for (int i = 0; i < kLaneElems; ++i) acc[i] = acc[i] + x[i];
         }
         const float so = block_max<B>(masked_absmax<Lanes>(acc, a.valid)) / C::kQmax;
-        const uint4 qo = C::quantize(acc, so);
+        const typename C::Vec qo = C::quantize(acc, so);
         if (a.valid) {
-            store_b128(codes_out + a.e0, qo);
+            C::store(codes_out, a.e0, qo);
             if (a.leads) scales_out[a.blk] = so;
         }
     }
@@ -331,17 +334,19 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
             const float s = scales[e / B];
             uint4 o;
             if constexpr (kSlot == 8) {
-                const uint2 c = *reinterpret_cast<const uint2*>(codes + e);
-                o.x = pack_bf16x2(C::value(c.x, 0) * s, C::value(c.x, 1) * s);
-                o.y = pack_bf16x2(C::value(c.x, 2) * s, C::value(c.x, 3) * s);
-                o.z = pack_bf16x2(C::value(c.y, 0) * s, C::value(c.y, 1) * s);
-                o.w = pack_bf16x2(C::value(c.y, 2) * s, C::value(c.y, 3) * s);
+                float c[8];
+                C::slot8(codes, e, c);
+                o.x = pack_bf16x2(c[0] * s, c[1] * s);
+                o.y = pack_bf16x2(c[2] * s, c[3] * s);
+                o.z = pack_bf16x2(c[4] * s, c[5] * s);
+                o.w = pack_bf16x2(c[6] * s, c[7] * s);
             } else {
-                const uint32_t c = *reinterpret_cast<const uint32_t*>(codes + e);
-                o.x = __builtin_bit_cast(uint32_t, C::value(c, 0) * s);
-                o.y = __builtin_bit_cast(uint32_t, C::value(c, 1) * s);
-                o.z = __builtin_bit_cast(uint32_t, C::value(c, 2) * s);
-                o.w = __builtin_bit_cast(uint32_t, C::value(c, 3) * s);
+                float c[4];
+                C::slot4(codes, e, c);
+                o.x = __builtin_bit_cast(uint32_t, c[0] * s);
+                o.y = __builtin_bit_cast(uint32_t, c[1] * s);
+                o.z = __builtin_bit_cast(uint32_t, c[2] * s);
+                o.w = __builtin_bit_cast(uint32_t, c[3] * s);
             }
             store_b128(out + e, o);
         }
@@ -720,6 +725,7 @@ hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void
 template <typename F>
 hipError_t dispatch_code(int code, F&& f) {
     if (code == kCodeE4M3) return f(TypeTag<E4M3Codes>{});
+    if (code == kCodeInt4) return f(TypeTag<Int4Codes>{});
     return f(TypeTag<Int8Codes>{});
 }
 

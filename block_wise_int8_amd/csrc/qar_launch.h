@@ -13,9 +13,9 @@ constexpr int kMaxRanks = 32;
 
 enum : int { kInBF16 = 0, kInF32 = 1 };
 enum : int { kOutNone = -1, kOutBF16 = 0, kOutF32 = 1 };
-// code format of the flat calls: int8 integers or FP8 E4M3 bytes (the row-
-// bounded path is int8 only)
-enum : int { kCodeInt8 = 0, kCodeE4M3 = 1 };
+// code format of the flat calls: int8 integers, FP8 E4M3 bytes, or 4-bit
+// integers two per byte (the row-bounded path is int8 only)
+enum : int { kCodeInt8 = 0, kCodeE4M3 = 1, kCodeInt4 = 2 };
 
 // Rank pointers travel in the kernel's argument segment (512 bytes).
 struct RankPtrs {

@@ -44,6 +44,11 @@ _SIGNATURES = {
     "qar_quantize_reduce_e4m3": [_vp, _int, _u32, _vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
     "qar_ring_step_e4m3": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize_e4m3": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
+    "qar_quantize_blocks_int4": [_vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_reduce_quantized_int4": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_quantize_reduce_int4": [_vp, _int, _u32, _vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
+    "qar_ring_step_int4": [_vp, _vp, _vp, _int, _sz, _u32, _vp, _vp, _vp],
+    "qar_dequantize_int4": [_vp, _vp, _sz, _u32, _vp, _int, _vp],
     "qar_status_string": [_int],
     "qar_last_error": [],
 }
@@ -126,8 +131,9 @@ def _ptrs(ts: list[torch.Tensor]):
 
 
 # code formats: the C function suffix and the torch dtype that holds the codes
-_INT8 = ("", torch.int8)
-_E4M3 = ("_e4m3", torch.uint8)
+_INT8 = ("", torch.int8, 1)
+_E4M3 = ("_e4m3", torch.uint8, 1)
+_INT4 = ("_int4", torch.uint8, 2)          # two codes per byte
 
 
 def _quantize(fmt, x, block, codes, scales, stream):
@@ -135,7 +141,7 @@ def _quantize(fmt, x, block, codes, scales, stream):
     _dev(x, "x")
     n = x.numel()
     if codes is None:
-        codes = torch.empty(n, dtype=fmt[1], device=x.device)
+        codes = torch.empty(n // fmt[2], dtype=fmt[1], device=x.device)
     if scales is None:
         scales = torch.empty(max(n // block, 1), dtype=torch.float32, device=x.device)
     _check(getattr(lib(), name)(x.data_ptr(), _dtype_code(x.dtype), n, block, _dev(codes, "codes").data_ptr(),
@@ -166,12 +172,12 @@ def _reduce(fmt, codes, scales, block, codes_out, scales_out, out, stream):
     name = "qar_reduce_quantized" + fmt[0]
     if len(codes) != len(scales) or not codes:
         raise ValueError("need one scales tensor per codes tensor, at least one rank")
-    n = codes[0].numel()
+    n = codes[0].numel() * fmt[2]            # elements
     for c, s in zip(codes, scales):
         _dev(c, "codes[r]"), _dev(s, "scales[r]")
     dev = codes[0].device
     if codes_out is None:
-        codes_out = torch.empty(n, dtype=fmt[1], device=dev)
+        codes_out = torch.empty(n // fmt[2], dtype=fmt[1], device=dev)
     if scales_out is None:
         scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
     optr, odt = _out_args(out)
@@ -190,6 +196,12 @@ def qar_reduce_quantized(codes: list[torch.Tensor], scales: list[torch.Tensor], 
     return _reduce(_INT8, codes, scales, block, codes_out, scales_out, out, stream)
 
 
+def qar_quantize_blocks_int4(x: torch.Tensor, block: int, codes: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None, stream=None):
+    """x (bf16/fp32) -> (4-bit codes packed two per byte, uint8[n/2]; scales fp32[n/block])."""
+    return _quantize(_INT4, x, block, codes, scales, stream)
+
+
 def qar_reduce_quantized_e4m3(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
                               codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
                               out: torch.Tensor | None = None, stream=None):
@@ -205,7 +217,7 @@ def _quantize_reduce(fmt, x_own, own, codes, scales, block, codes_out, scales_ou
     n = x_own.numel()
     dev = x_own.device
     if codes_out is None:
-        codes_out = torch.empty(n, dtype=fmt[1], device=dev)
+        codes_out = torch.empty(n // fmt[2], dtype=fmt[1], device=dev)
     if scales_out is None:
         scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=dev)
     optr, odt = _out_args(out)
@@ -222,6 +234,13 @@ def qar_quantize_reduce(x_own: torch.Tensor, own: int, codes: list[torch.Tensor]
     """Quantize x_own into codes[own]/scales[own] and reduce all ranks in the
     same pass -> (codes_out, scales_out); ``out`` gets the dequantized result."""
     return _quantize_reduce(_INT8, x_own, own, codes, scales, block, codes_out, scales_out, out, stream)
+
+
+def qar_reduce_quantized_int4(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int,
+                              codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None,
+                              out: torch.Tensor | None = None, stream=None):
+    """The one-shot reduce with packed 4-bit codes (uint8 tensors of n/2 bytes)."""
+    return _reduce(_INT4, codes, scales, block, codes_out, scales_out, out, stream)
 
 
 def qar_quantize_reduce_e4m3(x_own: torch.Tensor, own: int, codes: list[torch.Tensor],
@@ -257,9 +276,9 @@ def qar_reduce_quantized_pipelined(codes: list[torch.Tensor], scales: list[torch
 def _ring_step(fmt, codes_in, scales_in, local, block, codes_out, scales_out, stream):
     name = "qar_ring_step" + fmt[0]
     _dev(codes_in, "codes_in"), _dev(scales_in, "scales_in"), _dev(local, "local")
-    n = codes_in.numel()
+    n = local.numel()
     if codes_out is None:
-        codes_out = torch.empty(n, dtype=fmt[1], device=codes_in.device)
+        codes_out = torch.empty(n // fmt[2], dtype=fmt[1], device=codes_in.device)
     if scales_out is None:
         scales_out = torch.empty(max(n // block, 1), dtype=torch.float32, device=codes_in.device)
     _check(getattr(lib(), name)(codes_in.data_ptr(), scales_in.data_ptr(), local.data_ptr(),
@@ -275,6 +294,13 @@ def qar_ring_step(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.
     return _ring_step(_INT8, codes_in, scales_in, local, block, codes_out, scales_out, stream)
 
 
+def qar_quantize_reduce_int4(x_own: torch.Tensor, own: int, codes: list[torch.Tensor],
+                             scales: list[torch.Tensor], block: int, codes_out: torch.Tensor | None = None,
+                             scales_out: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None):
+    """The one-kernel step with packed 4-bit codes."""
+    return _quantize_reduce(_INT4, x_own, own, codes, scales, block, codes_out, scales_out, out, stream)
+
+
 def qar_ring_step_e4m3(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
                        codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
     """The ring step with FP8 E4M3 codes."""
@@ -284,7 +310,7 @@ def qar_ring_step_e4m3(codes_in: torch.Tensor, scales_in: torch.Tensor, local: t
 def _dequantize(fmt, codes, scales, block, out, out_dtype, stream):
     name = "qar_dequantize" + fmt[0]
     _dev(codes, "codes"), _dev(scales, "scales")
-    n = codes.numel()
+    n = codes.numel() * fmt[2]               # elements
     if out is None:
         out = torch.empty(n, dtype=out_dtype, device=codes.device)
     _check(getattr(lib(), name)(codes.data_ptr(), scales.data_ptr(), n, block, _dev(out, "out").data_ptr(),
@@ -298,10 +324,22 @@ def qar_dequantize(codes: torch.Tensor, scales: torch.Tensor, block: int, out: t
     return _dequantize(_INT8, codes, scales, block, out, out_dtype, stream)
 
 
+def qar_ring_step_int4(codes_in: torch.Tensor, scales_in: torch.Tensor, local: torch.Tensor, block: int,
+                       codes_out: torch.Tensor | None = None, scales_out: torch.Tensor | None = None, stream=None):
+    """The ring step with packed 4-bit codes."""
+    return _ring_step(_INT4, codes_in, scales_in, local, block, codes_out, scales_out, stream)
+
+
 def qar_dequantize_e4m3(codes: torch.Tensor, scales: torch.Tensor, block: int, out: torch.Tensor | None = None,
                         out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
     """FP8 E4M3 codes (uint8), scales -> out (bf16 or fp32)."""
     return _dequantize(_E4M3, codes, scales, block, out, out_dtype, stream)
+
+
+def qar_dequantize_int4(codes: torch.Tensor, scales: torch.Tensor, block: int, out: torch.Tensor | None = None,
+                        out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """Packed 4-bit codes (uint8, n/2 bytes), scales -> out (bf16 or fp32)."""
+    return _dequantize(_INT4, codes, scales, block, out, out_dtype, stream)
 
 
 def qar_reduce_unquantized(xs: list[torch.Tensor], out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -297,6 +297,38 @@ qar_status qar_ring_step_e4m3(const uint8_t* codes_in, const float* scales_in, c
 qar_status qar_dequantize_e4m3(const uint8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
                                qar_dtype out_dtype, void* stream);
 
+/*
+ * 4-bit integer codes.  The same calls with 4-bit codes, two per byte.  The
+ * pages name 4-bit communication quantization only through titles in their
+ * reference lists (SDP4Bit; Echo, error-compensated 4-bit tensor-parallel
+ * communication); libqar takes the int8 method at 4 bits:
+ *
+ *   scale  s   = absmax / 7              one IEEE binary32 division
+ *   code   q_i = 0 if s == 0, else clamp(rne(x_i / s), -7, 7)
+ *   value  y_i = (float)q_i * s
+ *
+ * Codes are packed: element 2k in the low nibble of byte k, element 2k+1 in
+ * the high nibble, two's complement (-8 is never produced); a buffer of n
+ * elements takes n/2 bytes.  A block-aligned sub-range starts block/2 bytes
+ * per block into the codes.  Alignment, aliasing (in place: the whole packed
+ * buffer and the scales), streams and errors are those of the int8 call of
+ * the same name; sizes of code buffers are n/2 bytes instead of n.
+ */
+qar_status qar_quantize_blocks_int4(const void* x, qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes,
+                                    float* scales, void* stream);
+qar_status qar_reduce_quantized_int4(const uint8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                     size_t n, uint32_t block, uint8_t* codes_out, float* scales_out, void* out,
+                                     qar_dtype out_dtype, void* stream);
+qar_status qar_quantize_reduce_int4(const void* x_own, qar_dtype dtype, uint32_t own, uint8_t* const* codes,
+                                    float* const* scales, uint32_t nranks, size_t n, uint32_t block,
+                                    uint8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                                    void* stream);
+qar_status qar_ring_step_int4(const uint8_t* codes_in, const float* scales_in, const void* local,
+                              qar_dtype dtype, size_t n, uint32_t block, uint8_t* codes_out, float* scales_out,
+                              void* stream);
+qar_status qar_dequantize_int4(const uint8_t* codes, const float* scales, size_t n, uint32_t block, void* out,
+                               qar_dtype out_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* qar_status_string(qar_status status);
 

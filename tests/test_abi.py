@@ -107,6 +107,28 @@ def test_e4m3_validation(L):
     assert L.qar_dequantize_e4m3(A, C, 256, 256, 0x80000, 5, None) == qar.QAR_ERR_UNSUPPORTED
 
 
+def test_int4_validation(L):
+    """4-bit code buffers hold n/2 bytes, and overlaps are judged on that
+    size.  Every call here fails a check, so nothing is launched."""
+    codes, scales = _arr(A, B_), _arr(C, D + 2)        # rank 1's scales misaligned
+    # codes_out 128 bytes after rank 0's codes: adjacent at n/2 = 128 bytes, so
+    # the check reaches rank 1 and reports its misaligned scales (with n bytes
+    # of codes it would have been an overlap)
+    assert L.qar_reduce_quantized_int4(codes, scales, 2, 256, 256, A + 128, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_MISALIGNED
+    assert L.qar_reduce_quantized(codes, scales, 2, 256, 256, A + 128, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_INVALID_ARG
+    # 64 bytes after: an overlap for 4-bit codes too
+    assert L.qar_reduce_quantized_int4(codes, scales, 2, 256, 256, A + 64, 0x60000, None, 0, None) \
+        == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_quantize_blocks_int4(A, 0, 256, 96, B_, C, None) == qar.QAR_ERR_UNSUPPORTED
+    assert L.qar_quantize_blocks_int4(A, 0, 256, 256, A + 256, C, None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_ring_step_int4(A, C, 0x80000, 0, 256, 96, B_, D, None) == qar.QAR_ERR_UNSUPPORTED
+    assert L.qar_dequantize_int4(A, C, 256, 256, A + 64, 0, None) == qar.QAR_ERR_INVALID_ARG
+    assert L.qar_quantize_reduce_int4(0x80000, 0, 2, _arr(A, B_), _arr(C, D), 2, 256, 256, 0x50000, 0x60000,
+                                      None, 0, None) == qar.QAR_ERR_INVALID_ARG
+
+
 def test_pipelined_validation(L):
     p = L.qar_reduce_quantized_pipelined
     codes, scales = _arr(A, B_), _arr(C, D)
