@@ -350,7 +350,7 @@ def main() -> int:
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
-        result["e4m3_codes"] = e4m3_bench(qar, torch, synth, dev, args.skew)
+        result["code_formats"] = code_formats_bench(qar, torch, synth, dev, args.skew)
         result["tiny"] = tiny_bench(qar, torch, synth, dev)
         result["row_bounded"] = rows_bench(qar, torch, dev)
 
@@ -581,12 +581,19 @@ def prefill_bench(qar, torch, synth, dev, skew):
     return res
 
 
-def e4m3_bench(qar, torch, synth, dev, skew):
-    """FP8 E4M3 codes against int8 codes on the outlier and prefill recipes
-    (data drawn on the GPU): time of the quantize, the reduce without output
-    and the one-kernel step on the outlier workload, and for both workloads
-    the error of each format's result against the exact (fp64) sum of the
-    bf16 inputs."""
+def code_formats_bench(qar, torch, synth, dev, skew):
+    """int8 against FP8 E4M3 and 4-bit codes on the outlier and prefill
+    recipes (data drawn on the GPU): for both workloads the error of each
+    format's one-shot result against the exact (fp64) sum of the bf16
+    inputs; on the outlier workload the time of the quantize, the reduce
+    without output and the one-kernel step of the E4M3 and 4-bit formats."""
+    fmts = {
+        "int8": (qar.qar_quantize_blocks, qar.qar_reduce_quantized, qar.qar_dequantize, qar.qar_quantize_reduce, 1),
+        "e4m3": (qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3, qar.qar_dequantize_e4m3,
+                 qar.qar_quantize_reduce_e4m3, 1),
+        "int4": (qar.qar_quantize_blocks_int4, qar.qar_reduce_quantized_int4, qar.qar_dequantize_int4,
+                 qar.qar_quantize_reduce_int4, 2),
+    }
     res = {"note": "error = dequantized fp32 result of the one-shot reduce minus the fp64 sum of the N bf16 "
                    "inputs, over every element; rms relative to the mean |sum|"}
     for key in ("outliers", "prefill"):
@@ -598,53 +605,52 @@ def e4m3_bench(qar, torch, synth, dev, skew):
             exact += x.double()
         mean_abs = exact.abs().mean().item()
         errs = {}
-        for fmt, quant, red, deq in (("int8", qar.qar_quantize_blocks, qar.qar_reduce_quantized,
-                                      qar.qar_dequantize),
-                                     ("e4m3", qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3,
-                                      qar.qar_dequantize_e4m3)):
+        for fmt, (quant, red, deq, _, _) in fmts.items():
             q = [quant(x, B) for x in xs]
             rc, rs = red([c for c, _ in q], [s for _, s in q], B)
-            y = deq(rc, rs, B, out_dtype=torch.float32).double()
-            d = (y - exact)
+            d = deq(rc, rs, B, out_dtype=torch.float32).double() - exact
             errs[fmt] = {"rms_over_mean_abs_sum": round((d.square().mean().sqrt() / mean_abs).item(), 6),
                          "max_abs": round(d.abs().max().item(), 6)}
-            del q, rc, rs, y, d
-        res[key] = {"workload": w.description, **errs,
-                    "rms_ratio_int8_over_e4m3": round(errs["int8"]["rms_over_mean_abs_sum"] /
-                                                      errs["e4m3"]["rms_over_mean_abs_sum"], 3)}
+            del q, rc, rs, d
+        res[key] = {"workload": w.description, **errs}
         if key == "outliers":
             nb = n // B
-            qbytes = n + 4 * nb
-            q = [qar.qar_quantize_blocks_e4m3(x, B) for x in xs]
-            nsets = 4
-            sets = []
-            for _ in range(nsets):
-                sets.append({"x": xs[0].clone(), "codes": _rank_block(torch, [c for c, _ in q], skew, dev),
-                             "scales": [s.clone() for _, s in q],
-                             "co": torch.empty(n, dtype=torch.uint8, device=dev),
-                             "so": torch.empty(nb, dtype=torch.float32, device=dev),
-                             "out": torch.empty(n, dtype=torch.bfloat16, device=dev)})
-            del q
+            timing = {}
+            for fmt in ("e4m3", "int4"):
+                quant, red, _, qred, per_byte = fmts[fmt]
+                qbytes = n // per_byte + 4 * nb
+                q = [quant(x, B) for x in xs]
+                nsets = 4
+                sets = []
+                for _ in range(nsets):
+                    sets.append({"x": xs[0].clone(), "codes": _rank_block(torch, [c for c, _ in q], skew, dev),
+                                 "scales": [s.clone() for _, s in q],
+                                 "co": torch.empty(n // per_byte, dtype=torch.uint8, device=dev),
+                                 "so": torch.empty(nb, dtype=torch.float32, device=dev),
+                                 "out": torch.empty(n, dtype=torch.bfloat16, device=dev)})
+                del q
 
-            def fq(i):
-                st = sets[i]
-                qar.qar_quantize_blocks_e4m3(st["x"], B, st["codes"][0], st["scales"][0])
+                def fq(i, quant=quant):
+                    st = sets[i]
+                    quant(st["x"], B, st["codes"][0], st["scales"][0])
 
-            def fr(i):
-                st = sets[i]
-                qar.qar_reduce_quantized_e4m3(st["codes"], st["scales"], B, st["co"], st["so"])
+                def fr(i, red=red):
+                    st = sets[i]
+                    red(st["codes"], st["scales"], B, st["co"], st["so"])
 
-            def fs(i):
-                st = sets[i]
-                qar.qar_quantize_reduce_e4m3(st["x"], 0, st["codes"], st["scales"], B, st["co"], st["so"],
-                                             out=st["out"])
-            res["timing_outliers"] = {
-                "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 100)),
-                "quantize_graph_replay": _rate(2 * n + qbytes, _graph_loop_us(torch, fq, nsets)),
-                "reduce_no_out": _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 100)),
-                "one_kernel_step": _rate(2 * n + (N + 1) * qbytes + 2 * n, _loop_us(torch, fs, nsets, 100)),
-            }
-            del sets
+                def fs(i, qred=qred):
+                    st = sets[i]
+                    qred(st["x"], 0, st["codes"], st["scales"], B, st["co"], st["so"], out=st["out"])
+                timing[fmt] = {
+                    "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 100, with_min=True)),
+                    "reduce_no_out": _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 100, with_min=True)),
+                    "one_kernel_step": _rate(2 * n + (N + 1) * qbytes + 2 * n,
+                                             _loop_us(torch, fs, nsets, 100, with_min=True)),
+                }
+                timing[fmt]["one_kernel_step"]["payload_GBps"] = round(
+                    N * n * 2 / (timing[fmt]["one_kernel_step"]["avg_us"] * 1e-6) / 1e9, 1)
+                del sets
+            res["timing_outliers"] = timing
         del xs, exact
         torch.cuda.empty_cache()
     return res

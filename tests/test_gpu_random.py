@@ -1,5 +1,5 @@
-"""Seeded random configurations through every flat call, int8 and E4M3
-codes, against the oracle bit for bit: rank count, block size, input type,
+"""Seeded random configurations through every flat call, int8, E4M3 and
+4-bit codes, against the oracle bit for bit: rank count, block size, input type,
 output type, size (whole blocks, from one block to several tiles) and the
 value distribution all drawn per case."""
 import numpy as np
@@ -50,7 +50,7 @@ def test_random_configuration(oracle_lib, case):
     nranks = int(rng.integers(1, 12))
     dtype = str(rng.choice(["bf16", "f32"]))
     n = int(rng.integers(1, 3 * 4096 // block + 3)) * block
-    codes_fmt = str(rng.choice(["int8", "e4m3"]))
+    codes_fmt = str(rng.choice(["int8", "e4m3", "int4"]))
     own = int(rng.integers(0, nranks))
     say(f"random case {case}: {codes_fmt} N={nranks} own={own} B={block} n={n} {dtype}")
     if codes_fmt == "int8":
@@ -59,6 +59,13 @@ def test_random_configuration(oracle_lib, case):
         o_quant, o_red, o_ring, o_deq = (oracle_lib.quantize, oracle_lib.reduce, oracle_lib.ring_step,
                                          oracle_lib.dequantize)
         view = lambda t: to_host(t)
+    elif codes_fmt == "int4":
+        quant, red, qred, ring, deq = (qar.qar_quantize_blocks_int4, qar.qar_reduce_quantized_int4,
+                                       qar.qar_quantize_reduce_int4, qar.qar_ring_step_int4, qar.qar_dequantize_int4)
+        o_quant, o_ring = oracle_lib.quantize_int4, oracle_lib.ring_step_int4
+        o_red = lambda c, s, b: oracle_lib.reduce_int4(c, s, b, n)
+        o_deq = lambda c, s, b, k: oracle_lib.dequantize_int4(c, s, b, n, k)
+        view = lambda t: to_host(t).view(np.uint8)
     else:
         quant, red, qred, ring, deq = (qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3,
                                        qar.qar_quantize_reduce_e4m3, qar.qar_ring_step_e4m3, qar.qar_dequantize_e4m3)
