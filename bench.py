@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--cpu-reps", type=int, default=4, help="oracle repetitions for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the reduce-only and ring-step lines")
+    p.add_argument("--preheat-ms", type=float, default=PREHEAT_MS,
+                   help="GPU time of untimed calls right before each timed region (0: none)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="only run 8 device-to-device copies of this many MiB (counter calibration) and exit")
     p.add_argument("--sweep", action="store_true",
@@ -142,7 +144,9 @@ def summarize_counters(d: str) -> int:
 
 
 def main() -> int:
+    global PREHEAT_MS
     args = parse()
+    PREHEAT_MS = args.preheat_ms
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -244,17 +248,18 @@ def main() -> int:
     def step(i):
         fused_step(sets[i % len(sets)])
 
+    # the GPU's steady state first (PREHEAT_MS of steps), then the W
+    # warm-up steps, then the timed region: K whole steps back to back, no
+    # events inside
+    i0 = _preheat(torch, step)
     for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # the timed region: K whole steps back to back, no events inside
+        step(i0 + i)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(i0 + args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -270,6 +275,7 @@ def main() -> int:
 
     reps = max(args.steps, 50)
     f_us, f_min = per_launch_us(fused_step, reps, with_min=True)
+    loop_preheat = _PREHEAT_CALLS[-1]
     q_us = per_launch_us(quantize_own, reps)
     r_us = per_launch_us(reduce_fused, reps)
 
@@ -324,8 +330,12 @@ def main() -> int:
             "algorithmic_bytes_per_launch": fused_bytes,
             "avg_launch_us": round(f_us, 3),
             "min_launch_us": round(f_min, 3),
-            "timing": f"{reps} back-to-back launches over the rotated sets, median of 5 event-bracketed segments",
+            "timing": (f"{reps} back-to-back launches over the rotated sets, median of 5 event-bracketed segments, "
+                       f"right behind {loop_preheat} untimed launches ({PREHEAT_MS:.0f} ms of preheat)"),
+            "preheat_launches": loop_preheat,
         },
+        "timed_region": {"preheat_steps": i0, "warmup_steps": args.warmup, "steps": args.steps,
+                         "note": f"{PREHEAT_MS:.0f} ms of steps, then the W warm-up steps, then the K timed ones"},
         "kernels": {
             "k_quantize_reduce (the step)": {"avg_us": round(f_us, 3), "bytes": fused_bytes,
                                              "GBps": round(achieved, 1)},
@@ -418,18 +428,58 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
             "note": "back-to-back launches over rotated buffer sets, out=NULL"}
 
 
+# Back-to-back launches of a kernel that does arithmetic besides streaming
+# HBM run slower for the first 10-25 ms after the GPU has been idle (the
+# step: 37.5 us per launch, up to 43 us a few milliseconds in, back to
+# 37.5 us after about 25 ms; a plain copy shows no such transient).  Every
+# timed region is therefore preceded, without a pause, by this many
+# milliseconds of the same calls.
+PREHEAT_MS = 50.0
+
+
+def _preheat(torch, fn, ms=None):
+    """Runs fn(i) back to back for about `ms` of GPU time (the count comes
+    from a short timed run) and returns the next index; the caller enqueues
+    its timed region right behind it, with no synchronisation."""
+    ms = PREHEAT_MS if ms is None else ms
+    if ms <= 0:
+        _PREHEAT_CALLS.append(0)
+        return 0
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(4):
+        fn(i)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(4, 20):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    est_us = max(a.elapsed_time(b) * 1e3 / 16, 1.0)
+    count = min(int(ms * 1e3 / est_us) + 1, 20000)
+    for i in range(20, 20 + count):
+        fn(i)
+    _PREHEAT_CALLS.append(20 + count)
+    return 20 + count
+
+
+_PREHEAT_CALLS = []   # calls made by each _preheat, in order (to split a kernel trace)
+
+
 def _segmented_us(torch, fn, reps, segments=5, with_min=False):
-    """fn(i) for i in range(reps) back to back on the current stream, with
-    an event at each of `segments` boundaries (no synchronisation between
-    them).  Returns the median over segments of the average time per call,
-    so a host-side pause that lets the GPU idle in one segment does not
-    count (and the fastest segment's, with_min=True)."""
+    """fn(i) for reps calls back to back on the current stream, with an
+    event at each of `segments` boundaries (no synchronisation between
+    them), right behind PREHEAT_MS of the same calls.  Returns the median
+    over segments of the average time per call, so a host-side pause that
+    lets the GPU idle in one segment does not count (and the fastest
+    segment's, with_min=True)."""
     stream = torch.cuda.current_stream()
     per = max(1, reps // segments)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(segments + 1)]
-    torch.cuda.synchronize()
+    i = _preheat(torch, fn)
+    if i == 0:
+        torch.cuda.synchronize()
     ev[0].record(stream)
-    i = 0
     for k in range(segments):
         for _ in range(per):
             fn(i)

@@ -158,10 +158,21 @@ __device__ __forceinline__ void store_dequantized_tile(typename C::Vec qo, float
     __builtin_amdgcn_wave_barrier();
 }
 
+// A line of zeros that the reduce reads in place of a rank slot it does not
+// use (past the last rank, or rank own, whose codes are made in registers),
+// so that every slot of a group is loaded without a branch.  Never written.
+__device__ __align__(64) uint32_t g_unused_slot[16];
+
 // The reduce over the tiles of one workgroup.  With OwnIn not void, rank
 // `own` is quantized from x_own in the same pass: its codes and scale are
 // written for the peers and the same register values enter the sum, so the
 // result equals a quantize followed by the plain reduce.
+//
+// With an own rank the loads of a group are unconditional (an unused slot
+// reads g_unused_slot), which lets the compiler wait for each rank's data on
+// its own instead of for the whole group: measured on the N = 8 step about
+// 3.5% faster than branching around the unused slots.  The plain reduce
+// keeps the branches; there the unconditional form measured 4% slower.
 template <int B, int OUT, typename Lanes, typename OwnIn, typename C>
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
@@ -190,7 +201,13 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
             float s[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                if (g + j < nranks && !(kOwn && g + j == own)) {
+                const bool used = g + j < nranks && !(kOwn && g + j == own);
+                if constexpr (kOwn) {
+                    const int8_t* c = used ? rp.codes[g + j] : reinterpret_cast<const int8_t*>(g_unused_slot);
+                    const float* sc = used ? rp.scales[g + j] : reinterpret_cast<const float*>(g_unused_slot);
+                    q[j] = C::load(c, used ? ld : 0);
+                    s[j] = sc[used ? blk : 0];
+                } else if (used) {
                     q[j] = C::load(rp.codes[g + j], ld);
                     s[j] = rp.scales[g + j][blk];
                 }
