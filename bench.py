@@ -356,6 +356,8 @@ def main() -> int:
         result["dequantize"] = dequantize_bench(qar, torch, sets, B, n, qbytes)
         result["unquantized_comparator"] = comparator_bench(qar, torch, synth, w, dev, args.skew,
                                                             result["reduce_only"]["avg_us"], f_us)
+        result["copy_reference"] = copy_reference(torch, fused_bytes, dev)
+        result["copy_reference"]["copy_time_over_step_time"] = round(result["copy_reference"]["avg_us"] / f_us, 4)
         result["ring_step"] = ring_bench(qar, torch, np, synth, dev)
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
         result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
@@ -887,7 +889,62 @@ def ring_bench(qar, torch, np, synth, dev):
     res = _rate(2 * (n + 4 * nb) + 2 * n, _loop_us(torch, fn, S, 200, warmup=5, with_min=True))
     res["graph_replay"] = _rate(2 * (n + 4 * nb) + 2 * n, _graph_loop_us(torch, fn, S, reps=4))
     res["workload"] = w.description
+    res["error_per_step"] = ring_errors(qar, torch, np, host, B, dev)
     return res
+
+
+def ring_errors(qar, torch, np, host, B, dev):
+    """The ring reduction of the ring workload on the GPU: q = quantize(x_0),
+    then q = ring_step(q, x_k) for k = 1..N-1.  After each step, the error of
+    the dequantized fp32 result against the fp64 partial sum x_0 + ... + x_k,
+    and its ratio to two bounds: the rigorous per-element one,
+    sum_j (s_j/2 + 2^-21 |p_j|) with p_j the fp32 values quantized at step j,
+    and the simple sum_j s_j/2 + 1e-6 |partial sum|."""
+    def f32(h):
+        return (h.reshape(-1).astype(np.uint32) << 16).view(np.float32)
+
+    def dev_bf16(h):
+        return torch.from_numpy(h.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    n = host[0].size
+    exact = f32(host[0]).astype(np.float64)
+    p = f32(host[0])
+    c, s = qar.qar_quantize_blocks(dev_bf16(host[0]), B)
+    rig = np.repeat(s.cpu().numpy().astype(np.float64), B)[:n] / 2 + 2.0 ** -21 * np.abs(p)
+    simple = np.repeat(s.cpu().numpy().astype(np.float64), B)[:n] / 2
+    steps = []
+    for k in range(1, len(host)):
+        y_prev = qar.qar_dequantize(c, s, B, out_dtype=torch.float32).cpu().numpy()
+        p = (y_prev + f32(host[k])).astype(np.float32)          # what this step quantizes
+        c, s = qar.qar_ring_step(c, s, dev_bf16(host[k]), B)
+        exact = exact + f32(host[k])
+        y = qar.qar_dequantize(c, s, B, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+        se = np.repeat(s.cpu().numpy().astype(np.float64), B)[:n]
+        rig = rig + se / 2 + 2.0 ** -21 * np.abs(p)
+        simple = simple + se / 2
+        err = np.abs(y - exact)
+        steps.append({"step": k, "max_abs": round(float(err.max()), 6), "mean_abs": round(float(err.mean()), 6),
+                      "rms": round(float(np.sqrt((err ** 2).mean())), 6),
+                      "max_err_over_bound": round(float((err / rig).max()), 6),
+                      "max_err_over_simple_bound": round(float((err / (simple + 1e-6 * np.abs(exact))).max()), 6)})
+    return steps
+
+
+def copy_reference(torch, nbytes, dev):
+    """A plain device-to-device copy (the runtime's blit kernel) moving the
+    same number of HBM bytes per launch as the step (nbytes/2 read, nbytes/2
+    written), over 8 rotated buffer pairs, timed like the kernels: the
+    achievable rate for this transfer size on this GPU."""
+    half = (nbytes // 2) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(8)]
+
+    def fn(i):
+        src, dst = pairs[i]
+        dst.copy_(src)
+    r = _rate(2 * half, _loop_us(torch, fn, len(pairs), 100, with_min=True))
+    r["what"] = f"torch copy_ (the runtime's blit kernel) of {half:,} bytes, 8 rotated buffer pairs"
+    return r
 
 
 def _cpu_threads() -> int:
