@@ -353,11 +353,48 @@ struct Int4Codes {
         }
         return make_uint2(nibbles8(w), nibbles8(w + 8));
     }
+    // code / 16 for the low nibble of byte BYTE of w: v_cvt_off_f32_i4 maps
+    // a 4-bit two's complement integer i to i/16, exactly; the SDWA byte
+    // select picks the nibble, so a code costs one instruction
+    template <int BYTE>
+    static __device__ __forceinline__ float sixteenth(uint32_t w) {
+        float f;
+        if constexpr (BYTE == 0)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f) : "v"(w));
+        else if constexpr (BYTE == 1)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(w));
+        else if constexpr (BYTE == 2)
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(w));
+        else
+            asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(w));
+        return f;
+    }
+    static __device__ __forceinline__ void dequantize8(uint32_t w, float s16, float* y) {
+        const uint32_t hi = w >> 4; // odd codes into the low nibbles
+        y[0] = sixteenth<0>(w) * s16;
+        y[1] = sixteenth<0>(hi) * s16;
+        y[2] = sixteenth<1>(w) * s16;
+        y[3] = sixteenth<1>(hi) * s16;
+        y[4] = sixteenth<2>(w) * s16;
+        y[5] = sixteenth<2>(hi) * s16;
+        y[6] = sixteenth<3>(w) * s16;
+        y[7] = sixteenth<3>(hi) * s16;
+    }
+    // y = code * s.  For s <= 2^123, (code/16) * (16 s) is the same real
+    // product (16 s is exact and finite), so it rounds to the same binary32
+    // value, signed zeros included; larger, infinite or NaN scales take the
+    // integer conversion.
     static __device__ __forceinline__ void dequantize(Vec q, float s, float (&y)[kLaneElems]) {
+        if (s <= 0x1p123f) {
+            const float s16 = s * 16.0f;
+            dequantize8(q.x, s16, y);
+            dequantize8(q.y, s16, y + 8);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            y[k] = value(q.x, k) * s;
-            y[8 + k] = value(q.y, k) * s;
+            for (int k = 0; k < 8; ++k) {
+                y[k] = value(q.x, k) * s;
+                y[8 + k] = value(q.y, k) * s;
+            }
         }
     }
     static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {

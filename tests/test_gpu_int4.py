@@ -103,6 +103,37 @@ def test_dequantize_int4_parity(oracle_lib, out, block):
     _same_out(to_host(y), oracle_lib.dequantize_int4(packed, scales, block, n, out), out, "dequantized")
 
 
+@pytest.mark.parametrize("nranks", [1, 2])
+def test_reduce_int4_every_byte_every_scale_range(oracle_lib, nranks):
+    """Arbitrary packed bytes (all 256 values, so -8 too) reduced with scales
+    from the subnormal range up to 2^124-2^125 (both sides of 2^123, where
+    the kernels' code-to-float conversion changes), zero and tiny scales
+    included; the sums stay finite."""
+    block = 64
+    n = ragged_n(block)
+    rng = np.random.default_rng(4242 + nranks)
+    top = 125 if nranks == 1 else 124
+    codes, scales = [], []
+    for r in range(nranks):
+        packed = rng.integers(0, 256, n // 2).astype(np.uint8)
+        packed[:256] = np.arange(256, dtype=np.uint8)
+        sc = np.exp2(rng.uniform(-149, top, n // block)).astype(np.float32)
+        sc[rng.integers(0, n // block, 8)] = 0.0
+        sc[:4] = np.float32(2.0 ** 123), np.nextafter(np.float32(2.0 ** 123), np.float32(np.inf)), \
+            np.float32(2.0 ** (top - 0.01)), np.float32(2.0 ** -149)
+        codes.append(packed)
+        scales.append(sc)
+    say(f"int4 reduce every byte N={nranks}")
+    out = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    oc, os_ = qar.qar_reduce_quantized_int4([to_dev(c) for c in codes], [to_dev(s) for s in scales], block,
+                                            out=out)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce_int4(codes, scales, block, n)
+    assert_same_codes(_packed(oc), wc, "packed codes")
+    assert_same_f32(to_host(os_), ws, "scales")
+    assert_same_f32(to_host(out), oracle_lib.dequantize_int4(wc, ws, block, n, "f32"), "fp32 out")
+
+
 def _ranks(o, xs, block):
     qs = [o.quantize_int4(x, block) for x in xs]
     return [q[0] for q in qs], [q[1] for q in qs]
@@ -155,10 +186,13 @@ def test_quantize_reduce_int4_parity(oracle_lib, nranks, own, dtype):
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("block", qar.BLOCK_SIZES)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_ring_step_int4_parity(oracle_lib, dtype, block, in_place):
+@pytest.mark.parametrize("outlier", [SUM_OUTLIER, 1.6e38])
+def test_ring_step_int4_parity(oracle_lib, dtype, block, in_place, outlier):
+    """The second outlier value gives scales above 2^123, where the kernels
+    convert codes to float another way."""
     n = ragged_n(block)
     make = mixed_bf16 if dtype == "bf16" else mixed_f32
-    x0, x1 = make(21 + block, n, block, SUM_OUTLIER), make(22 + block, n, block, SUM_OUTLIER)
+    x0, x1 = make(21 + block, n, block, outlier), make(22 + block, n, block, outlier)
     c0, s0 = oracle_lib.quantize_int4(x0, block)
     dc, ds = to_dev(c0), to_dev(s0)
     if in_place:
