@@ -75,7 +75,9 @@ def parse():
     p.add_argument("--skew", type=int, default=4096,
                    help="bytes added to the stride between rank code buffers in one allocation "
                         "(multiple of 16); -1 = one allocation per rank")
-    p.add_argument("--cpu-reps", type=int, default=4, help="oracle repetitions for the CPU baseline")
+    p.add_argument("--cpu-reps", type=int, default=4, help="least oracle repetitions for the CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="about this much wall time for the CPU baseline on T threads (a quarter on one)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the reduce-only and ring-step lines")
     p.add_argument("--preheat-ms", type=float, default=PREHEAT_MS,
@@ -978,17 +980,24 @@ def cpu_baseline(args, np, w, host, set0, torch):
                            [s0] + [s[lo // B:hi // B] for s in scales[1:]], B)
         return c0, oc, o.dequantize(oc, os_, B, kind)
 
-    reps = max(1, args.cpu_reps)
+    # repetitions: at least --cpu-reps, and enough for about --cpu-seconds
+    # of wall time on T threads (a quarter of it on one thread)
     t0 = time.perf_counter()
-    for _ in range(reps):
+    c0, oc, y = step(0, w.n)
+    dt1 = time.perf_counter() - t0
+    reps1 = max(1, args.cpu_reps, int(args.cpu_seconds / 4 / dt1))
+    t0 = time.perf_counter()
+    for _ in range(reps1):
         c0, oc, y = step(0, w.n)
-    dt1 = (time.perf_counter() - t0) / reps
+    dt1 = (time.perf_counter() - t0) / reps1
 
     T = _cpu_threads()
     nb = w.n // B
     cuts = [(nb * k // T) * B for k in range(T + 1)]
     with ThreadPoolExecutor(T) as pool:
+        t0 = time.perf_counter()
         list(pool.map(lambda k: step(cuts[k], cuts[k + 1]), range(T)))           # warm the pool
+        reps = max(1, args.cpu_reps, int(args.cpu_seconds / (time.perf_counter() - t0)))
         t0 = time.perf_counter()
         for _ in range(reps):
             parts = list(pool.map(lambda k: step(cuts[k], cuts[k + 1]), range(T)))
@@ -1013,7 +1022,7 @@ def cpu_baseline(args, np, w, host, set0, torch):
                       f"{w.nranks} ranks, dequantize) on {T} host threads, each on its own block range; "
                       f"{dtT:.3f} s per step",
             "single_thread": {"value": round(payload / dt1 / 1e9, 3), "unit": "GB/s", "cores": 1,
-                              "seconds_per_step": round(dt1, 4)},
+                              "seconds_per_step": round(dt1, 4), "repetitions": reps1},
             "threads_agree_with_single_thread": bool(same_split),
             "gpu_output_matches_oracle": same}
 

@@ -5,13 +5,15 @@
 // "technical framework": blocks (step 1), dynamic per-block quantization to
 // INT8 (step 2, with the run-time range of "key design" item 1), reduction of
 // quantized contributions (step 3), dequantization (step 4).  The flat kernels
-// take the code format as a policy (Int8Codes, or E4M3Codes for the FP8
-// variant of the TACO page, "Why FP8?"); both are one byte per element.  The
-// arithmetic each kernel performs is spelled out in include/qar.h.
+// take the code format as a policy: Int8Codes; E4M3Codes for the FP8 variant
+// of the TACO page, "Why FP8?" (one byte per element as well); Int4Codes, the
+// int8 rules at 4 bits with two codes per byte.  The arithmetic each kernel
+// performs is spelled out in include/qar.h.
 //
-// Every kernel streams HBM once: 16-byte loads and stores per lane, a block's
-// absmax by DPP inside its lanes, the requantization fused behind the
-// reduction so the fp32 sum never leaves registers.  A workgroup walks tiles
+// Every kernel streams HBM once: 16-byte loads and stores per lane (8-byte
+// code accesses for 4-bit codes), a block's absmax by DPP inside its lanes,
+// the requantization fused behind the reduction so the fp32 sum never leaves
+// registers.  A workgroup walks tiles
 // of 4096 elements with a grid-stride loop (the grid is capped, the loop
 // covers any n).
 #include <type_traits>
