@@ -245,3 +245,44 @@ def test_int4_workload(oracle_lib, key):
     err = np.abs(deq - exact)
     assert np.all(err <= bnd), f"{key}: 4-bit bound violated, worst ratio {np.max(err / bnd)}"
     say(f"int4 {key}: bit-exact; max err/bound {np.max(err / bnd):.3f}")
+
+
+def test_int4_beyond_2_pow_31_elements(oracle_lib):
+    """4-bit quantize, dequantize, reduce and the one-kernel step (N = 2) at
+    n above 2**31 (code buffers above 2**30 bytes), checked against the
+    oracle on sampled blocks and the last ones."""
+    from gpu_util import TILE
+    block = 256
+    n = (1 << 31) + 3 * TILE + 7 * block
+    say(f"int4 large n={n}")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(79)
+    x0 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 1.0, generator=g)
+    x1 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_(0.0, 2.0, generator=g)
+    c1, s1 = qar.qar_quantize_blocks_int4(x1, block)
+    y1 = qar.qar_dequantize_int4(c1, s1, block, out_dtype=torch.bfloat16)
+    c0 = torch.empty(n // 2, dtype=torch.uint8, device="cuda:0")
+    s0 = torch.empty(n // block, dtype=torch.float32, device="cuda:0")
+    fc, fs = qar.qar_quantize_reduce_int4(x0, 0, [c0, c1], [s0, s1], block)
+    q0, qs0 = qar.qar_quantize_blocks_int4(x0, block)
+    rc, rs = qar.qar_reduce_quantized_int4([q0, c1], [qs0, s1], block)
+    torch.cuda.synchronize()
+    nb = n // block
+    rng = np.random.default_rng(9)
+    picks = np.concatenate([rng.choice(nb, 2000, replace=False), np.arange(nb - 40, nb)])
+    pk = torch.from_numpy(picks).cuda()
+    idx = torch.from_numpy((picks[:, None] * block + np.arange(block)).reshape(-1)).cuda()
+    cidx = torch.from_numpy((picks[:, None] * (block // 2) + np.arange(block // 2)).reshape(-1)).cuda()
+    q = [oracle_lib.quantize_int4(to_host(x[idx]), block) for x in (x0, x1)]
+    m = idx.numel()
+    assert_same_codes(_packed(c1[cidx]), q[1][0], "codes")
+    assert_same_f32(to_host(s1[pk]), q[1][1], "scales")
+    assert_same_bits16(to_host(y1[idx]), oracle_lib.dequantize_int4(q[1][0], q[1][1], block, m, "bf16"),
+                       "dequantized")
+    wc, ws = oracle_lib.reduce_int4([a for a, _ in q], [b for _, b in q], block, m)
+    assert_same_codes(_packed(c0[cidx]), q[0][0], "own codes")
+    for c, s_, what in ((fc, fs, "step"), (rc, rs, "reduce")):
+        assert_same_codes(_packed(c[cidx]), wc, f"{what} codes")
+        assert_same_f32(to_host(s_[pk]), ws, f"{what} scales")
+    del x0, x1, c0, c1, s0, s1, y1, fc, fs, q0, qs0, rc, rs
+    torch.cuda.empty_cache()
