@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_ring_step(const int8_t* codes_in, 
 // a wavefront owns the store slots at elements 8L + 512j (bf16, j = 0..1) or
 // 4L + 256j (fp32, j = 0..3) of the wave's 1024-element tile and reads the
 // 8 or 4 codes of each slot directly (8 or 4 bytes, 512 or 256 bytes
-// contiguous per load instruction).
+// contiguous per load instruction; half that for 4-bit codes).
 template <int B, typename Out, typename C = Int8Codes>
 __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restrict__ codes,
                                                          const float* __restrict__ scales, size_t n,
