@@ -103,9 +103,10 @@ def _counter_kernels(N, n, B):
             ("k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", N * qb, qb + 2 * n)]
 
 
-def summarize_counters(d: str) -> int:
+def summarize_counters(d: str, out: str | None = None) -> int:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's kernels,
-    scaled by what the same counters read for a plain 1 GiB device copy."""
+    scaled by what the same counters read for a plain 1 GiB device copy;
+    written to `out` (default: the committed summary under profiles/)."""
     import csv
     import statistics
 
@@ -139,7 +140,7 @@ def summarize_counters(d: str) -> int:
                            "fetch_factor": round(ff, 5), "write_factor": round(fw, 5)},
            "hbm_bytes_per_launch": top["hbm_read_bytes"] + top["hbm_write_bytes"],
            "kernels": rows}
-    with open(counters_path(w.key), "w") as f:
+    with open(out or counters_path(w.key), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
     return 0
