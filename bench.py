@@ -317,6 +317,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.key}: {w.description}",
             "nranks": N, "elements_per_rank": n, "block": B, "input_dtype": w.dtype,
+            "seed": w.seed, "input_sha256_16": [synth.sha256(h)[:16] for h in host],
             "step": "one kernel: quantize own buffer + reduce/requantize/dequantize of N contributions",
             "buffer_sets": args.sets, "footprint_bytes": set_bytes * args.sets,
             "rank_stride_bytes": stride if args.skew >= 0 else None,
