@@ -206,7 +206,10 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
  *     0..N-1 requantizes the sum in place into codes_work[0]/scales_work[0]
  *     and writes its dequantized value to out.  The last rank's quantize
  *     runs inside that reduce (qar_quantize_reduce) when N > 1; the results
- *     are the same bits.
+ *     are the same bits.  With nchunks = N the chunks are the N slices of a
+ *     two-shot AllReduce's reduce-scatter (the TACO page, "system-level
+ *     kernel fusion and overlap": reduce-scatter, then all-gather); its
+ *     all-gather forwards the requantized codes unchanged.
  *   QAR_SCHEDULE_RING: chunk c starts at rank s = c mod N, as the chunk
  *     rank s injects first in a ring: quantize(x_s), then ring steps adding
  *     x_{s+1}, ..., x_{s+N-1} (ranks mod N) in place in codes_work[0] /
