@@ -98,7 +98,8 @@ def parse():
 # the outlier workload's kernels; N ranks, n elements, block B, bf16 in/out
 def _counter_kernels(N, n, B):
     qb = n + 4 * (n // B)
-    return [("k_quantize_reduce<256, 0, unsigned short, qar::Int8Codes>", 2 * n + (N - 1) * qb, 2 * qb + 2 * n),
+    return [("k_quantize_reduce<256, 0, unsigned short, qar::Int8Codes, true>", 2 * n + (N - 1) * qb,
+             2 * qb + 2 * n),
             ("k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", 2 * n, qb),
             ("k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", N * qb, qb + 2 * n)]
 

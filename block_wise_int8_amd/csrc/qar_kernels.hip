@@ -170,12 +170,15 @@ __device__ __align__(64) uint32_t g_unused_slot[16];
 // written for the peers and the same register values enter the sum, so the
 // result equals a quantize followed by the plain reduce.
 //
-// With an own rank the loads of a group are unconditional (an unused slot
-// reads g_unused_slot), which lets the compiler wait for each rank's data on
-// its own instead of for the whole group: measured on the N = 8 step about
-// 3.5% faster than branching around the unused slots.  The plain reduce
-// keeps the branches; there the unconditional form measured 4% slower.
-template <int B, int OUT, typename Lanes, typename OwnIn, typename C>
+// kDense: every slot of a load group is loaded, an unused one (rank own,
+// whose codes are made in registers, or past the last rank) reading
+// g_unused_slot, which lets the compiler wait for each rank's data on its own
+// instead of for the whole group.  Measured on the step (own rank, N ranks):
+// 3-5% faster for N = 5..8 and 16, but each slot past the last rank costs a
+// load, so with 1-4 ranks in the last group (N = 2: 16% slower) the loads
+// branch around the unused slots instead; the launcher picks by N.  The
+// plain reduce always branches (the dense form measured 4% slower there).
+template <int B, int OUT, typename Lanes, typename OwnIn, typename C, bool kDense = false>
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                              const OwnIn* __restrict__ x_own, int own,
@@ -204,7 +207,7 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const bool used = g + j < nranks && !(kOwn && g + j == own);
-                if constexpr (kOwn) {
+                if constexpr (kDense) {
                     const int8_t* c = used ? rp.codes[g + j] : reinterpret_cast<const int8_t*>(g_unused_slot);
                     const float* sc = used ? rp.scales[g + j] : reinterpret_cast<const float*>(g_unused_slot);
                     q[j] = C::load(c, used ? ld : 0);
@@ -288,14 +291,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, La
                                          nullptr, nullptr);
 }
 
-template <int B, int OUT, typename In, typename C = Int8Codes>
+template <int B, int OUT, typename In, typename C = Int8Codes, bool kDense = true>
 __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restrict__ x_own, int own,
                                                               int8_t* own_codes, float* own_scales,
                                                               RankPtrs rp, int nranks, FlatLanes<B> lanes,
                                                               int8_t* codes_out, float* scales_out,
                                                               void* __restrict__ out, uint32_t ntiles) {
-    reduce_tiles<B, OUT, FlatLanes<B>, In, C>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own, own,
-                                              own_codes, own_scales);
+    reduce_tiles<B, OUT, FlatLanes<B>, In, C, kDense>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own,
+                                                      own, own_codes, own_scales);
 }
 
 // ---------------------------------------------------------------------------
@@ -885,12 +888,19 @@ hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const
         return dispatch_block(block, [&](auto bc) {
             constexpr int B = decltype(bc)::value;
             const FlatLanes<B> lanes{n};
+            // dense loads unless the last group of 8 ranks has 1-4 of them
+            const bool dense = nranks % 8 == 0 || nranks % 8 >= 5;
             auto go = [&](auto oc, auto in_tag) {
                 constexpr int OUT = decltype(oc)::value;
                 using In = typename decltype(in_tag)::type;
-                hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C>), dim3(g.blocks), dim3(kThreads), 0, st,
-                                   static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
-                                   codes_out, scales_out, out, g.ntiles);
+                if (dense)
+                    hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C, true>), dim3(g.blocks), dim3(kThreads), 0,
+                                       st, static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks,
+                                       lanes, codes_out, scales_out, out, g.ntiles);
+                else
+                    hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C, false>), dim3(g.blocks), dim3(kThreads), 0,
+                                       st, static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks,
+                                       lanes, codes_out, scales_out, out, g.ntiles);
             };
             auto with_in = [&](auto oc) {
                 if (in_kind == kInBF16)
