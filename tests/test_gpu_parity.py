@@ -190,7 +190,7 @@ def test_quantize_reduce_parity(oracle_lib, nranks, own, dtype, block):
 
 
 @pytest.mark.parametrize("nstreams", [1, 4])
-@pytest.mark.parametrize("nchunks", [1, 3, 8, 16, 64])
+@pytest.mark.parametrize("nchunks", [1, 3, 8, 16, 32, 64])
 def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
     block, nranks = 64, 5
     n = ragged_n(block, tiles=6)
