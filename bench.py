@@ -316,13 +316,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+f32",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {
             "workload": f"{w.key}: {w.description}",
             "nranks": N, "elements_per_rank": n, "block": B, "input_dtype": w.dtype,
             "seed": w.seed, "input_sha256_16": [synth.sha256(h)[:16] for h in host],
             "step": "one kernel: quantize own buffer + reduce/requantize/dequantize of N contributions",
+            "codes": f"int8 with one fp32 scale per block of {B} (arithmetic in fp32)",
             "buffer_sets": args.sets, "footprint_bytes": set_bytes * args.sets,
             "rank_stride_bytes": stride if args.skew >= 0 else None,
             "parallelism": "one GPU's share",
