@@ -376,6 +376,7 @@ def main() -> int:
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
         result["code_formats"] = code_formats_bench(qar, torch, synth, dev, args.skew)
         result["tiny"] = tiny_bench(qar, torch, synth, dev)
+        result["one_gpu_share"] = share_bench(qar, torch, synth, dev, args.skew)
         result["row_bounded"] = rows_bench(qar, torch, dev)
 
     if not args.no_cpu_baseline:
@@ -422,6 +423,53 @@ def sweep(qar, torch, synth, dev, skew) -> int:
         del sets
         torch.cuda.empty_cache()
     return 0
+
+
+def share_bench(qar, torch, synth, dev, skew):
+    """One GPU's share of an 8-GPU one-shot AllReduce of the outlier
+    workload: the GPU reduces its 1/8 slice of blocks, so every kernel sees
+    N = 8 slices of n/8 = 2,097,152 elements.  The step (quantize its own
+    slice, reduce the 8 slices, bf16 out) and the reduce without output, all
+    slices resident in this GPU's HBM (over xGMI the 7 peer slices would be
+    read from the peers); sets rotated over >= 1 GiB.  Eager calls are bound
+    by the binding's host work at this size, so HIP graph replays are
+    reported beside them."""
+    w0 = synth.WORKLOADS["outliers"]
+    N, B = w0.nranks, w0.block
+    n = w0.n // N
+    nb = n // B
+    qbytes = n + 4 * nb
+    x = [synth.device_rank(w0, r, dev)[:n].clone() for r in range(N)]
+    q = [qar.qar_quantize_blocks(x[r], B) for r in range(N)]
+    per_set = (N + 2) * qbytes + 4 * n
+    nsets = max(2, -(-(1 << 30) // per_set))
+    sets = []
+    for _ in range(nsets):
+        sets.append({"x": x[0].clone(), "c": _rank_block(torch, [c for c, _ in q], skew, dev),
+                     "s": [s.clone() for _, s in q], "co": torch.empty(n, dtype=torch.int8, device=dev),
+                     "so": torch.empty(nb, dtype=torch.float32, device=dev),
+                     "out": torch.empty(n, dtype=torch.bfloat16, device=dev)})
+    del q
+
+    def fr(i):
+        st = sets[i]
+        qar.qar_reduce_quantized(st["c"], st["s"], B, st["co"], st["so"])
+
+    def fs(i):
+        st = sets[i]
+        qar.qar_quantize_reduce(st["x"], 0, st["c"], st["s"], B, st["co"], st["so"], out=st["out"])
+    step_bytes = 2 * n + (N + 1) * qbytes + 2 * n
+    res = {"workload": f"one GPU's slice of an 8-GPU one-shot AllReduce: N={N} x {n:,} bf16, block {B}",
+           "buffer_sets": nsets,
+           "step": _rate(step_bytes, _loop_us(torch, fs, nsets, 100, with_min=True)),
+           "reduce_no_out": _rate((N + 1) * qbytes, _loop_us(torch, fr, nsets, 100, with_min=True))}
+    res["step"]["graph_replay"] = _rate(step_bytes, _graph_loop_us(torch, lambda i: fs(i % nsets), nsets,
+                                                                   per_graph=nsets))
+    res["reduce_no_out"]["graph_replay"] = _rate((N + 1) * qbytes, _graph_loop_us(
+        torch, lambda i: fr(i % nsets), nsets, per_graph=nsets))
+    del sets, x
+    torch.cuda.empty_cache()
+    return res
 
 
 def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
