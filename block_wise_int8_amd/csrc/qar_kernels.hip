@@ -6,9 +6,9 @@
 // INT8 (step 2, with the run-time range of "key design" item 1), reduction of
 // quantized contributions (step 3), dequantization (step 4).  The flat kernels
 // take the code format as a policy: Int8Codes; E4M3Codes for the FP8 variant
-// of the TACO page, "Why FP8?" (one byte per element as well); Int4Codes, the
-// int8 rules at 4 bits with two codes per byte.  The arithmetic each kernel
-// performs is spelled out in include/qar.h.
+// of the TACO page, section 2.A "Waarom FP8?" (one byte per element as
+// well); Int4Codes, the int8 rules at 4 bits with two codes per byte.  The
+// arithmetic each kernel performs is spelled out in include/qar.h.
 //
 // Every kernel streams HBM once: 16-byte loads and stores per lane (8-byte
 // code accesses for 4-bit codes), a block's absmax by DPP inside its lanes,

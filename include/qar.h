@@ -207,8 +207,8 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
  *     and writes its dequantized value to out.  The last rank's quantize
  *     runs inside that reduce (qar_quantize_reduce) when N > 1; the results
  *     are the same bits.  With nchunks = N the chunks are the N slices of a
- *     two-shot AllReduce's reduce-scatter (the TACO page, "system-level
- *     kernel fusion and overlap": reduce-scatter, then all-gather); its
+ *     two-shot AllReduce's reduce-scatter (the TACO page, section 2.B
+ *     item 3, kernel fusion and overlap: reduce-scatter, then all-gather); its
  *     all-gather forwards the requantized codes unchanged.
  *   QAR_SCHEDULE_RING: chunk c starts at rank s = c mod N, as the chunk
  *     rank s injects first in a ring: quantize(x_s), then ring steps adding
@@ -264,10 +264,11 @@ qar_status qar_dequantize_rows(const int8_t* codes, const float* scales, size_t 
 
 /*
  * FP8 E4M3 codes.  The same calls with 8-bit floating-point codes in place
- * of int8 integers: the format the TACO page argues for ("TACO:
- * Tensor-parallel Adaptive COmmunication compression", page summary,
- * section "Why FP8?"), with the per-block scale of its "Dual-Scale
- * quantization" section that brings the block into FP8's range Q_max (only
+ * of int8 integers: the format the TACO page argues for ("TACO: Efficient
+ * Communication Compression of Intermediate Tensors for Scalable
+ * Tensor-Parallel LLM Training", page summary in Dutch, section 2.A "Waarom
+ * FP8?", why FP8), with the per-block scale of its section 2.B item 2
+ * "Dual-Scale (DS) Quantization" that brings the block into FP8's range Q_max (only
  * that scale; no rotation).  E4M3 is the OCP format: sign, 4 exponent bits
  * with bias 7, 3 mantissa bits, subnormals (m/8) * 2^-6, no infinity, codes
  * 0x7F and 0xFF NaN (never produced), largest finite value 448.

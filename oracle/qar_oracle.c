@@ -274,10 +274,11 @@ void oracle_f32_to_bf16(const float* in, size_t n, uint16_t* out)
 
 /* ------------------------------------------------------------------------
  * FP8 E4M3 codes: the same block-wise method with 8-bit floating-point codes
- * instead of integers.  "TACO: Tensor-parallel Adaptive COmmunication
- * compression" (page summary), section "Why FP8?": the E4M3 format's
+ * instead of integers.  "TACO: Efficient Communication Compression of
+ * Intermediate Tensors for Scalable Tensor-Parallel LLM Training" (page
+ * summary, in Dutch), section 2.A "Waarom FP8?" (why FP8): the E4M3 format's
  * exponential spacing keeps precision for the many small values and range
- * for the outliers; section "Dual-Scale quantization": a per-block scale
+ * for the outliers; section 2.B item 2, "Dual-Scale (DS) Quantization": a per-block scale
  * brings the block into FP8's dynamic range, Q_max.  Only that single
  * post-scale is taken here (no rotation, no pre-scale).
  *

@@ -147,8 +147,9 @@ def ring_step(codes: list[int], scales: list[Fraction], local: list[Fraction], b
 
 
 # ---------------------------------------------------------------------------
-# FP8 E4M3 codes ("TACO" page, sections "Why FP8?" and "Dual-Scale
-# quantization"; format from the OCP 8-bit floating point specification).
+# FP8 E4M3 codes (the TACO page, sections 2.A "Waarom FP8?" and 2.B item 2
+# "Dual-Scale (DS) Quantization"; format from the OCP 8-bit floating point
+# specification).
 # Every finite E4M3 value is listed from the format's fields; the nearest one
 # is found by scanning the whole list, ties to the code with an even
 # mantissa.

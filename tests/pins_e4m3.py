@@ -9,9 +9,11 @@ oracle disagrees with:
     symmetry, power-of-two scaling, zero blocks),
   - the error bounds (1e) of ``oracle/bounds.py``.
 
-Method: "TACO: Tensor-parallel Adaptive COmmunication compression" (page
-summary), sections "Why FP8?" (E4M3 codes) and "Dual-Scale quantization"
-(a per-block scale that brings the block into FP8's range Q_max), applied to
+Method: "TACO: Efficient Communication Compression of Intermediate Tensors
+for Scalable Tensor-Parallel LLM Training" (page summary, in Dutch), sections
+2.A "Waarom FP8?" (why FP8: E4M3 codes) and 2.B item 2 "Dual-Scale (DS)
+Quantization" (a per-block scale that brings the block into FP8's range
+Q_max), applied to
 the block-wise quantized reduce of "EQuARX: Efficient Quantized AllReduce in
 XLA ...", section "technical framework" steps 1-4.
 """
