@@ -53,6 +53,25 @@ def test_random_configuration(oracle_lib, case):
     codes_fmt = str(rng.choice(["int8", "e4m3", "int4"]))
     own = int(rng.integers(0, nranks))
     say(f"random case {case}: {codes_fmt} N={nranks} own={own} B={block} n={n} {dtype}")
+    _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own)
+
+
+@pytest.mark.parametrize("size", ["one block", "tile minus a block", "one tile", "tile plus a block"])
+@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("codes_fmt", ["int8", "e4m3", "int4"])
+def test_edge_sizes(oracle_lib, codes_fmt, block, size):
+    """Sizes at the edges of the tiling: a single block (one lane group of a
+    wave), one block short of a 4,096-element tile, exactly one tile, and one
+    block into a second tile, through every flat call."""
+    n = {"one block": block, "tile minus a block": 4096 - block, "one tile": 4096,
+         "tile plus a block": 4096 + block}[size]
+    rng = np.random.default_rng(20_000 + n + block)
+    dtype = "bf16" if (n // block) % 2 else "f32"
+    say(f"edge size: {codes_fmt} B={block} n={n} {dtype}")
+    _run_case(oracle_lib, rng, block, 3, dtype, n, codes_fmt, 1)
+
+
+def _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own):
     if codes_fmt == "int8":
         quant, red, qred, ring, deq = (qar.qar_quantize_blocks, qar.qar_reduce_quantized, qar.qar_quantize_reduce,
                                        qar.qar_ring_step, qar.qar_dequantize)
