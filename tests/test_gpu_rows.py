@@ -135,3 +135,39 @@ def test_rows_unaligned_pointers_take_the_general_path(oracle_lib):
     wc, ws = _oracle_quantize_rows(oracle_lib, x, block)
     assert_same_codes(to_host(c), wc, "codes")
     assert_same_f32(to_host(s), ws, "scales")
+
+
+EDGE_SHAPES = [(1, 16, 64), (3, 1, 64), (2, 17, 256), (1, 4096 + 16, 256), (4, 64, 64), (2, 255, 256)]
+
+
+@pytest.mark.parametrize("rows,row_len,block", EDGE_SHAPES)
+def test_rows_edge_shapes(oracle_lib, rows, row_len, block):
+    """Edge shapes: one-element rows, one row of a single lane group, one row
+    just past a tile, rows of exactly one block and one element short of a
+    block -- quantize, dequantize, the reduce (N = 3, bf16 out) and a ring
+    step, row by row against the oracle."""
+    rng = np.random.default_rng(rows * 1000 + row_len)
+    xs = [synth.f32_to_bf16_bits((rng.normal(0, 1, (rows, row_len)) * np.exp(rng.normal(0, 4, (rows, 1))))
+                                 .astype(np.float32)).reshape(rows, row_len) for _ in range(3)]
+    say(f"rows edge {rows}x{row_len} B={block}")
+    qs = [qar.qar_quantize_rows(_dev2(x, rows, row_len), block) for x in xs]
+    y = qar.qar_dequantize_rows(qs[0][0], qs[0][1], rows, row_len, block, out_dtype=torch.bfloat16)
+    o = torch.empty(rows * row_len, device="cuda:0", dtype=torch.bfloat16)
+    oc, os_ = qar.qar_reduce_quantized_rows([q[0] for q in qs], [q[1] for q in qs], rows, row_len, block, out=o)
+    gc_, gs_ = qar.qar_ring_step_rows(qs[0][0], qs[0][1], _dev2(xs[1], rows, row_len), block)
+    torch.cuda.synchronize()
+    per_rank = [_split(*_oracle_quantize_rows(oracle_lib, x, block), rows, row_len, block) for x in xs]
+    for r, (q, p) in enumerate(zip(qs, per_rank)):
+        assert_same_codes(to_host(q[0]), p[0].reshape(-1), f"rank {r} codes")
+        assert_same_f32(to_host(q[1]), p[1].reshape(-1), f"rank {r} scales")
+    want_y = np.concatenate([oracle_lib.dequantize(per_rank[0][0][r], per_rank[0][1][r], block, "bf16")
+                             for r in range(rows)])
+    assert_same_bits16(to_host(y).reshape(-1), want_y, "dequantized")
+    red = [oracle_lib.reduce([p[0][r] for p in per_rank], [p[1][r] for p in per_rank], block) for r in range(rows)]
+    assert_same_codes(to_host(oc), np.concatenate([c for c, _ in red]), "reduce codes")
+    assert_same_f32(to_host(os_), np.concatenate([s for _, s in red]), "reduce scales")
+    assert_same_bits16(to_host(o), np.concatenate([oracle_lib.dequantize(c, s, block, "bf16") for c, s in red]),
+                       "reduce out")
+    ring = [oracle_lib.ring_step(per_rank[0][0][r], per_rank[0][1][r], xs[1][r], block) for r in range(rows)]
+    assert_same_codes(to_host(gc_), np.concatenate([c for c, _ in ring]), "ring codes")
+    assert_same_f32(to_host(gs_), np.concatenate([s for _, s in ring]), "ring scales")
