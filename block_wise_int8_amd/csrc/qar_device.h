@@ -126,9 +126,19 @@ constexpr float kRoundMagic = 12582912.0f;
 // stays below 1/2.  Smaller scales take the IEEE division.
 constexpr float kFastQuotientMinScale = 0x1p-100f;
 
-__device__ __forceinline__ uint32_t code_bits_of(float t) {
-    t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+// On the fast path the clamp to [-Q, Q] can never change a code, so it is
+// left out there.  s = fl(m/Q) is normal, hence s >= (m/Q)(1 - 2^-24), and
+// every |x| <= m (m the block's absmax) has |x/s| <= Q/(1 - 2^-24) < Q + 2^-16
+// for Q <= 127; Q + 2^-16 is a binary32 value, so the correctly rounded
+// quotient is at most Q + 2^-16 and rounds to at most Q.  A subnormal s can
+// lie far below m/Q (m = 190 * 2^-149 gives s = 2^-149 and a quotient of
+// 190), so the IEEE-division path clamps.
+__device__ __forceinline__ uint32_t code_bits_of(float t) { // |t| < 127.5
     return __builtin_bit_cast(uint32_t, t + kRoundMagic);
+}
+
+__device__ __forceinline__ uint32_t clamped_code_bits_of(float t) {
+    return code_bits_of(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f));
 }
 
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -150,7 +160,7 @@ __device__ __forceinline__ uint4 quantize16(const float (&v)[kLaneElems], float 
         }
     } else if (s != 0.0f) {
 #pragma unroll
-        for (int i = 0; i < kLaneElems; ++i) w[i] = code_bits_of(v[i] / s);
+        for (int i = 0; i < kLaneElems; ++i) w[i] = clamped_code_bits_of(v[i] / s);
     } else {
 #pragma unroll
         for (int i = 0; i < kLaneElems; ++i) w[i] = __builtin_bit_cast(uint32_t, kRoundMagic);
@@ -342,7 +352,7 @@ struct Int4Codes {
                 float y = v[i] * r;
                 const float e = __builtin_fmaf(-y, s, v[i]);
                 y = __builtin_fmaf(e, r, y);
-                w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(y, -kQmax, kQmax) + kRoundMagic);
+                w[i] = __builtin_bit_cast(uint32_t, y + kRoundMagic); // no clamp needed (see code_bits_of)
             }
         } else if (s != 0.0f) {
 #pragma unroll

@@ -530,7 +530,7 @@ __device__ __forceinline__ void quantize4(const float (&v)[kRowSlots], float s, 
         }
     } else if (s != 0.0f) {
 #pragma unroll
-        for (int t = 0; t < kRowSlots; ++t) q[t] = (int8_t)(code_bits_of(v[t] / s) & 0xFFu);
+        for (int t = 0; t < kRowSlots; ++t) q[t] = (int8_t)(clamped_code_bits_of(v[t] / s) & 0xFFu);
     } else {
 #pragma unroll
         for (int t = 0; t < kRowSlots; ++t) q[t] = 0;
