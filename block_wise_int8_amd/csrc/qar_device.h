@@ -207,9 +207,10 @@ __device__ __forceinline__ void dequantize16(uint4 q, float s, float (&y)[kLaneE
 // the type of a lane's 16 codes (Vec) and how to load, store, make and read
 // them.  Byte-wide formats (int8, E4M3) keep a lane's codes in one 16-byte
 // vector at byte offset e0; the 4-bit format packs them into 8 bytes at e0/2.
-// slot8/slot4 read the codes of 8 or 4 consecutive elements starting at e
-// (a multiple of 8 or 4) from global memory or LDS, for the kernels that
-// write their output in contiguous 16-byte slots.
+// scaled8/scaled4 give code * s (one binary32 product each) for the 8 or 4
+// consecutive elements starting at e (a multiple of 8 or 4), their codes
+// read from global memory or LDS, for the kernels that write their output
+// in contiguous 16-byte slots.
 
 // EQuARX's integers: q = clamp(rne(x/s), -127, 127), s = absmax / 127.
 struct Int8Codes {
@@ -225,18 +226,18 @@ struct Int8Codes {
     static __device__ __forceinline__ void dequantize(Vec q, float s, float (&y)[kLaneElems]) {
         dequantize16(q, s, y);
     }
-    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+    static __device__ __forceinline__ void scaled8(const int8_t* c, size_t e, float s, float (&y)[8]) {
         const uint2 w = *reinterpret_cast<const uint2*>(c + e);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[k] = value(w.x, k);
-            v[4 + k] = value(w.y, k);
+            y[k] = value(w.x, k) * s;
+            y[4 + k] = value(w.y, k) * s;
         }
     }
-    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+    static __device__ __forceinline__ void scaled4(const int8_t* c, size_t e, float s, float (&y)[4]) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
+        for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
     }
 };
 
@@ -307,18 +308,18 @@ struct E4M3Codes {
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[4 * j + k] = value(w[j], k) * s;
     }
-    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+    static __device__ __forceinline__ void scaled8(const int8_t* c, size_t e, float s, float (&y)[8]) {
         const uint2 w = *reinterpret_cast<const uint2*>(c + e);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[k] = value(w.x, k);
-            v[4 + k] = value(w.y, k);
+            y[k] = value(w.x, k) * s;
+            y[4 + k] = value(w.y, k) * s;
         }
     }
-    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+    static __device__ __forceinline__ void scaled4(const int8_t* c, size_t e, float s, float (&y)[4]) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
+        for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
     }
 };
 
@@ -407,15 +408,29 @@ struct Int4Codes {
             }
         }
     }
-    static __device__ __forceinline__ void slot8(const int8_t* c, size_t e, float (&v)[8]) {
+    // the same products for 8 or 4 codes (4 or 2 bytes), widened as in dequantize
+    static __device__ __forceinline__ void scaled8(const int8_t* c, size_t e, float s, float (&y)[8]) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e / 2);
+        if (s <= 0x1p123f) {
+            dequantize8(w, s * 16.0f, y);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = value(w, k);
+            for (int k = 0; k < 8; ++k) y[k] = value(w, k) * s;
+        }
     }
-    static __device__ __forceinline__ void slot4(const int8_t* c, size_t e, float (&v)[4]) {
+    static __device__ __forceinline__ void scaled4(const int8_t* c, size_t e, float s, float (&y)[4]) {
         const uint32_t w = *reinterpret_cast<const uint16_t*>(c + e / 2);
+        if (s <= 0x1p123f) {
+            const float s16 = s * 16.0f;
+            const uint32_t hi = w >> 4; // codes 1 and 3 into the low nibbles of bytes 0 and 1
+            y[0] = sixteenth<0>(w) * s16;
+            y[1] = sixteenth<0>(hi) * s16;
+            y[2] = sixteenth<1>(w) * s16;
+            y[3] = sixteenth<1>(hi) * s16;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = value(w, k);
+            for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
+        }
     }
 };
 

@@ -131,28 +131,26 @@ __device__ __forceinline__ void store_dequantized_tile(typename C::Vec qo, float
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int e = 512 * j + 8 * lane; // element within the wave tile
-            float c[8];
-            C::slot8(codes, e, c);
-            const float s = lds_scales[e / B];
+            float y[8];
+            C::scaled8(codes, e, lds_scales[e / B], y);
             uint4 o;
-            o.x = pack_bf16x2(c[0] * s, c[1] * s);
-            o.y = pack_bf16x2(c[2] * s, c[3] * s);
-            o.z = pack_bf16x2(c[4] * s, c[5] * s);
-            o.w = pack_bf16x2(c[6] * s, c[7] * s);
+            o.x = pack_bf16x2(y[0], y[1]);
+            o.y = pack_bf16x2(y[2], y[3]);
+            o.z = pack_bf16x2(y[4], y[5]);
+            o.w = pack_bf16x2(y[6], y[7]);
             if (wave0 + e < n) store_b128(static_cast<uint16_t*>(out) + wave0 + e, o);
         }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 256 * j + 4 * lane;
-            float c[4];
-            C::slot4(codes, e, c);
-            const float s = lds_scales[e / B];
+            float y[4];
+            C::scaled4(codes, e, lds_scales[e / B], y);
             uint4 o;
-            o.x = __builtin_bit_cast(uint32_t, c[0] * s);
-            o.y = __builtin_bit_cast(uint32_t, c[1] * s);
-            o.z = __builtin_bit_cast(uint32_t, c[2] * s);
-            o.w = __builtin_bit_cast(uint32_t, c[3] * s);
+            o.x = __builtin_bit_cast(uint32_t, y[0]);
+            o.y = __builtin_bit_cast(uint32_t, y[1]);
+            o.z = __builtin_bit_cast(uint32_t, y[2]);
+            o.w = __builtin_bit_cast(uint32_t, y[3]);
             if (wave0 + e < n) store_b128(static_cast<float*>(out) + wave0 + e, o);
         }
     }
@@ -356,19 +354,19 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
             const float s = scales[e / B];
             uint4 o;
             if constexpr (kSlot == 8) {
-                float c[8];
-                C::slot8(codes, e, c);
-                o.x = pack_bf16x2(c[0] * s, c[1] * s);
-                o.y = pack_bf16x2(c[2] * s, c[3] * s);
-                o.z = pack_bf16x2(c[4] * s, c[5] * s);
-                o.w = pack_bf16x2(c[6] * s, c[7] * s);
+                float y[8];
+                C::scaled8(codes, e, s, y);
+                o.x = pack_bf16x2(y[0], y[1]);
+                o.y = pack_bf16x2(y[2], y[3]);
+                o.z = pack_bf16x2(y[4], y[5]);
+                o.w = pack_bf16x2(y[6], y[7]);
             } else {
-                float c[4];
-                C::slot4(codes, e, c);
-                o.x = __builtin_bit_cast(uint32_t, c[0] * s);
-                o.y = __builtin_bit_cast(uint32_t, c[1] * s);
-                o.z = __builtin_bit_cast(uint32_t, c[2] * s);
-                o.w = __builtin_bit_cast(uint32_t, c[3] * s);
+                float y[4];
+                C::scaled4(codes, e, s, y);
+                o.x = __builtin_bit_cast(uint32_t, y[0]);
+                o.y = __builtin_bit_cast(uint32_t, y[1]);
+                o.z = __builtin_bit_cast(uint32_t, y[2]);
+                o.w = __builtin_bit_cast(uint32_t, y[3]);
             }
             store_b128(out + e, o);
         }
