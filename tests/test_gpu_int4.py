@@ -97,6 +97,9 @@ def test_dequantize_int4_parity(oracle_lib, out, block):
     packed[:256] = np.arange(256, dtype=np.uint8)
     scales = np.exp2(rng.uniform(-149, 124, n // block)).astype(np.float32)
     scales[0] = 0.0
+    # both sides of 2^123, where the kernels' code-to-float conversion changes
+    scales[1:4] = np.float32(2.0 ** 123), np.nextafter(np.float32(2.0 ** 123), np.float32(np.inf)), \
+        np.float32(2.0 ** 123.99)
     y = qar.qar_dequantize_int4(to_dev(packed), to_dev(scales), block,
                                 out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
     torch.cuda.synchronize()
@@ -125,13 +128,18 @@ def test_reduce_int4_every_byte_every_scale_range(oracle_lib, nranks):
         scales.append(sc)
     say(f"int4 reduce every byte N={nranks}")
     out = torch.empty(n, dtype=torch.float32, device="cuda:0")
-    oc, os_ = qar.qar_reduce_quantized_int4([to_dev(c) for c in codes], [to_dev(s) for s in scales], block,
-                                            out=out)
+    out16 = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    oc, os_ = qar.qar_reduce_quantized_int4(dc, ds, block, out=out)
+    oc16, os16 = qar.qar_reduce_quantized_int4(dc, ds, block, out=out16)
     torch.cuda.synchronize()
     wc, ws = oracle_lib.reduce_int4(codes, scales, block, n)
+    assert float(ws.max()) > 2.0 ** 123                 # the fused output's slow widening runs too
     assert_same_codes(_packed(oc), wc, "packed codes")
     assert_same_f32(to_host(os_), ws, "scales")
     assert_same_f32(to_host(out), oracle_lib.dequantize_int4(wc, ws, block, n, "f32"), "fp32 out")
+    assert_same_codes(_packed(oc16), wc, "packed codes (bf16 out)")
+    assert_same_bits16(to_host(out16), oracle_lib.dequantize_int4(wc, ws, block, n, "bf16"), "bf16 out")
 
 
 def _ranks(o, xs, block):
