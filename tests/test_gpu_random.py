@@ -2,6 +2,8 @@
 4-bit codes, against the oracle bit for bit: rank count, block size, input type,
 output type, size (whole blocks, from one block to several tiles) and the
 value distribution all drawn per case."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,8 @@ from gpu_util import assert_same_bits16, assert_same_codes, assert_same_f32, say
 
 pytestmark = pytest.mark.gpu
 
-CASES = 40
+# seeds 10,000 .. 10,000 + CASES - 1; QAR_RANDOM_CASES widens the sweep
+CASES = int(os.environ.get("QAR_RANDOM_CASES", "200"))
 
 
 @pytest.fixture(scope="module", autouse=True)
