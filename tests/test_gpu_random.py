@@ -50,7 +50,8 @@ def _same_out(got, want, dtype, what):
 def test_random_configuration(oracle_lib, case):
     rng = np.random.default_rng(10_000 + case)
     block = int(rng.choice([64, 128, 256]))
-    nranks = int(rng.integers(1, 12))
+    # mostly one or two load groups of 8 ranks, sometimes up to the limit (four)
+    nranks = int(rng.integers(1, 12)) if rng.random() < 0.8 else int(rng.integers(12, qar.QAR_MAX_RANKS + 1))
     dtype = str(rng.choice(["bf16", "f32"]))
     n = int(rng.integers(1, 3 * 4096 // block + 3)) * block
     codes_fmt = str(rng.choice(["int8", "e4m3", "int4"]))
