@@ -1,6 +1,8 @@
 """Row-bounded blocks ([rows, row_len], the block grid restarting at each
 row) through the C ABI, against the oracle applied row by row (the oracle
 quantizes any block length and a partial last block).  Bit-exact."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -169,5 +171,58 @@ def test_rows_edge_shapes(oracle_lib, rows, row_len, block):
     assert_same_bits16(to_host(o), np.concatenate([oracle_lib.dequantize(c, s, block, "bf16") for c, s in red]),
                        "reduce out")
     ring = [oracle_lib.ring_step(per_rank[0][0][r], per_rank[0][1][r], xs[1][r], block) for r in range(rows)]
+    assert_same_codes(to_host(gc_), np.concatenate([c for c, _ in ring]), "ring codes")
+    assert_same_f32(to_host(gs_), np.concatenate([s for _, s in ring]), "ring scales")
+
+
+RANDOM_ROW_CASES = int(os.environ.get("QAR_RANDOM_CASES", "200")) // 4
+
+
+@pytest.mark.parametrize("case", range(RANDOM_ROW_CASES))
+def test_rows_random_configuration(oracle_lib, case):
+    """Seeded random row shapes (row lengths with and without a partial last
+    block, on and off the 16-element lane grid), block size, rank count,
+    input and output types, through every row call against the oracle row by
+    row."""
+    rng = np.random.default_rng(30_000 + case)
+    block = int(rng.choice([64, 128, 256]))
+    rows = int(rng.integers(1, 24))
+    row_len = int(rng.integers(1, 3 * block + 1)) * (16 if rng.random() < 0.5 else 1)
+    nranks = int(rng.integers(1, 10))
+    kind = str(rng.choice(["bf16", "f32"]))
+    out_kind = str(rng.choice(["none", "bf16", "f32"]))
+    say(f"rows random case {case}: {rows}x{row_len} B={block} N={nranks} {kind} out={out_kind}")
+    xs = []
+    for _ in range(nranks):
+        v = (rng.normal(0, 1, (rows, row_len)) * np.exp(rng.normal(0, 4, (rows, 1)))).astype(np.float32)
+        xs.append(synth.f32_to_bf16_bits(v).reshape(rows, row_len) if kind == "bf16" else v)
+    qs = [qar.qar_quantize_rows(_dev2(x, rows, row_len), block) for x in xs]
+    o = None if out_kind == "none" else torch.empty(rows * row_len, device="cuda:0",
+                                                    dtype=torch.bfloat16 if out_kind == "bf16" else torch.float32)
+    oc, os_ = qar.qar_reduce_quantized_rows([q[0] for q in qs], [q[1] for q in qs], rows, row_len, block, out=o)
+    gc_, gs_ = qar.qar_ring_step_rows(qs[0][0], qs[0][1], _dev2(xs[-1], rows, row_len), block)
+    y = qar.qar_dequantize_rows(oc, os_, rows, row_len, block,
+                                out_dtype=torch.bfloat16 if kind == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    per_rank = [_split(*_oracle_quantize_rows(oracle_lib, x, block), rows, row_len, block) for x in xs]
+    for r, (q, p) in enumerate(zip(qs, per_rank)):
+        assert_same_codes(to_host(q[0]), p[0].reshape(-1), f"rank {r} codes")
+        assert_same_f32(to_host(q[1]), p[1].reshape(-1), f"rank {r} scales")
+    red = [oracle_lib.reduce([p[0][r] for p in per_rank], [p[1][r] for p in per_rank], block) for r in range(rows)]
+    wc, ws = np.concatenate([c for c, _ in red]), np.concatenate([s for _, s in red])
+    assert_same_codes(to_host(oc), wc, "reduce codes")
+    assert_same_f32(to_host(os_), ws, "reduce scales")
+    if o is not None:
+        want = np.concatenate([oracle_lib.dequantize(c, s, block, out_kind) for c, s in red])
+        if out_kind == "bf16":
+            assert_same_bits16(to_host(o), want, "fused out")
+        else:
+            assert_same_f32(to_host(o), want, "fused out")
+    want_y = np.concatenate([oracle_lib.dequantize(c, s, block, kind) for c, s in red])
+    if kind == "bf16":
+        assert_same_bits16(to_host(y).reshape(-1), want_y, "dequantized")
+    else:
+        assert_same_f32(to_host(y).reshape(-1), want_y, "dequantized")
+    ring = [oracle_lib.ring_step(per_rank[0][0][r], per_rank[0][1][r], xs[-1][r], block) for r in range(rows)]
     assert_same_codes(to_host(gc_), np.concatenate([c for c, _ in ring]), "ring codes")
     assert_same_f32(to_host(gs_), np.concatenate([s for _, s in ring]), "ring scales")
