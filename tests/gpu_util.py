@@ -76,3 +76,35 @@ def assert_same_bits16(got: np.ndarray, want: np.ndarray, what: str) -> None:
 
 def say(*a) -> None:
     print(*a, flush=True)
+
+
+def oracle_allreduce(o, xs, block, schedule, nchunks):
+    """The simulated AllReduce composed from oracle calls: one-shot (quantize
+    every rank, reduce, dequantize) or ring by chunks (chunk c of
+    ceil(nb / nchunks) blocks starts at rank c mod N).  Returns the result's
+    codes, scales and dequantized values."""
+    n = xs[0].size
+    kind = "bf16" if xs[0].dtype == np.uint16 else "f32"
+    if schedule == "one_shot":
+        qs = [o.quantize(x, block) for x in xs]
+        c, s = o.reduce([q[0] for q in qs], [q[1] for q in qs], block)
+        return c, s, o.dequantize(c, s, block, kind)
+    nb = n // block
+    chunks = min(nchunks, nb)
+    per = -(-nb // chunks)
+    codes = np.empty(n, np.int8)
+    scales = np.empty(nb, np.float32)
+    out = np.empty(n, xs[0].dtype)
+    N = len(xs)
+    for ch in range(chunks):
+        b0 = ch * per
+        if b0 >= nb:
+            break
+        b1 = min(nb, b0 + per)
+        sl = slice(b0 * block, b1 * block)
+        s0 = ch % N
+        c, s = o.quantize(xs[s0][sl], block)
+        for k in range(1, N):
+            c, s = o.ring_step(c, s, xs[(s0 + k) % N][sl], block)
+        codes[sl], scales[b0:b1], out[sl] = c, s, o.dequantize(c, s, block, kind)
+    return codes, scales, out

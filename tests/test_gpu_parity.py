@@ -11,7 +11,7 @@ import torch
 import golden_cases as gc
 from block_wise_int8_amd import qar, synth
 from gpu_util import (SUM_OUTLIER, TILE, assert_same_bits16, assert_same_codes, assert_same_f32, f32_bits,
-                      mixed_bf16, mixed_f32, ragged_n, say, to_dev, to_host)
+                      mixed_bf16, mixed_f32, oracle_allreduce, ragged_n, say, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -260,34 +260,6 @@ def test_reduce_unquantized_parity(oracle_lib, nranks, dtype):
 # the whole AllReduce on one GPU
 
 
-def _oracle_allreduce(o, xs, block, schedule, nchunks):
-    n = xs[0].size
-    kind = "bf16" if xs[0].dtype == np.uint16 else "f32"
-    if schedule == "one_shot":
-        qs = [o.quantize(x, block) for x in xs]
-        c, s = o.reduce([q[0] for q in qs], [q[1] for q in qs], block)
-        return c, s, o.dequantize(c, s, block, kind)
-    nb = n // block
-    chunks = min(nchunks, nb)
-    per = -(-nb // chunks)
-    codes = np.empty(n, np.int8)
-    scales = np.empty(nb, np.float32)
-    out = np.empty(n, xs[0].dtype)
-    N = len(xs)
-    for ch in range(chunks):
-        b0 = ch * per
-        if b0 >= nb:
-            break
-        b1 = min(nb, b0 + per)
-        sl = slice(b0 * block, b1 * block)
-        s0 = ch % N
-        c, s = o.quantize(xs[s0][sl], block)
-        for k in range(1, N):
-            c, s = o.ring_step(c, s, xs[(s0 + k) % N][sl], block)
-        codes[sl], scales[b0:b1], out[sl] = c, s, o.dequantize(c, s, block, kind)
-    return codes, scales, out
-
-
 @pytest.mark.parametrize("schedule", ["one_shot", "ring"])
 @pytest.mark.parametrize("nranks,nchunks,nstreams,dtype,block", [
     (1, 2, 2, "bf16", 128), (2, 1, 1, "bf16", 256), (3, 3, 2, "bf16", 128), (4, 4, 4, "bf16", 256), (4, 16, 4, "f32", 64),
@@ -304,7 +276,7 @@ def test_allreduce_simulated(oracle_lib, schedule, nranks, nchunks, nstreams, dt
     streams = [torch.cuda.Stream() for _ in range(nstreams)]
     out = qar.qar_allreduce_simulated(dx, block, schedule, nchunks, streams, workspace=(wc, ws))
     torch.cuda.synchronize()
-    c, s, y = _oracle_allreduce(oracle_lib, xs, block, schedule, nchunks)
+    c, s, y = oracle_allreduce(oracle_lib, xs, block, schedule, nchunks)
     assert_same_codes(to_host(wc[0]), c, "result codes")
     assert_same_f32(to_host(ws[0]), s, "result scales")
     if dtype == "bf16":

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from block_wise_int8_amd import qar, synth
-from gpu_util import assert_same_bits16, assert_same_codes, assert_same_f32, say, to_dev, to_host
+from gpu_util import assert_same_bits16, assert_same_codes, assert_same_f32, oracle_allreduce, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,38 @@ def _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own):
     rgc, rgs = o_ring(wq[0][0], wq[0][1], xs[-1], block)
     assert_same_codes(view(gc_), rgc, "ring codes")
     assert_same_f32(to_host(gs_), rgs, "ring scales")
+
+
+@pytest.mark.parametrize("case", range(CASES // 4))
+def test_random_pipelined_and_simulated(oracle_lib, case):
+    """Seeded random chunk counts and stream counts through the pipelined
+    reduce and the simulated AllReduce (one-shot and ring), against the
+    oracle's reduce and its chunk-by-chunk composition."""
+    rng = np.random.default_rng(40_000 + case)
+    block = int(rng.choice([64, 128, 256]))
+    nranks = int(rng.integers(1, 10))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    n = int(rng.integers(1, 3 * 4096 // block + 3)) * block
+    nchunks = int(rng.integers(1, 2 * (n // block) + 2))        # sometimes more chunks than blocks
+    nstreams = int(rng.integers(1, 5))
+    schedule = str(rng.choice(["one_shot", "ring"]))
+    say(f"random pipelined case {case}: N={nranks} B={block} n={n} {dtype} chunks={nchunks} "
+        f"streams={nstreams} {schedule}")
+    xs = [_draw(rng, n, block, dtype) for _ in range(nranks)]
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    q = [qar.qar_quantize_blocks(to_dev(x), block) for x in xs]
+    pc, ps = qar.qar_reduce_quantized_pipelined([c for c, _ in q], [s for _, s in q], block, nchunks, streams)
+    nwork = nranks if schedule == "one_shot" else 1
+    wc = [torch.empty(n, dtype=torch.int8, device="cuda:0") for _ in range(nwork)]
+    ws = [torch.empty(n // block, dtype=torch.float32, device="cuda:0") for _ in range(nwork)]
+    out = qar.qar_allreduce_simulated([to_dev(x) for x in xs], block, schedule, nchunks, streams,
+                                      workspace=(wc, ws))
+    torch.cuda.synchronize()
+    wq = [oracle_lib.quantize(x, block) for x in xs]
+    rc, rs = oracle_lib.reduce([c for c, _ in wq], [s for _, s in wq], block)
+    assert_same_codes(to_host(pc), rc, "pipelined codes")
+    assert_same_f32(to_host(ps), rs, "pipelined scales")
+    c, s, y = oracle_allreduce(oracle_lib, xs, block, schedule, nchunks)
+    assert_same_codes(to_host(wc[0]), c, "simulated result codes")
+    assert_same_f32(to_host(ws[0]), s, "simulated result scales")
+    _same_out(to_host(out), y, dtype, "simulated result")
