@@ -268,11 +268,10 @@ struct E4M3Codes {
         default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
         }
     }
+    // Four quotients of magnitude at most 448 + 2^-15 into four codes.  The
+    // conversion rounds 448 + 2^-15 to 448 (0x7E) but turns anything from 465
+    // up into NaN (0x7F), so larger quotients must be clamped first.
     static __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
-        a = __builtin_amdgcn_fmed3f(a, -kQmax, kQmax);
-        b = __builtin_amdgcn_fmed3f(b, -kQmax, kQmax);
-        c = __builtin_amdgcn_fmed3f(c, -kQmax, kQmax);
-        d = __builtin_amdgcn_fmed3f(d, -kQmax, kQmax);
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
         return (uint32_t)w;
@@ -285,12 +284,14 @@ struct E4M3Codes {
             for (int i = 0; i < kLaneElems; ++i) {
                 float y = v[i] * r;
                 const float e = __builtin_fmaf(-y, s, v[i]);
-                // x = -0 gives e = +0 and +0 + -0 = +0: put the sign back
+                // x = -0 gives e = +0 and +0 + -0 = +0: put the sign back.
+                // No clamp: as for int8 (code_bits_of), a normal s bounds the
+                // rounded quotient by Q + 2^-15 here.
                 t[i] = __builtin_copysignf(__builtin_fmaf(e, r, y), v[i]);
             }
         } else if (s != 0.0f) {
 #pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) t[i] = v[i] / s;
+            for (int i = 0; i < kLaneElems; ++i) t[i] = __builtin_amdgcn_fmed3f(v[i] / s, -kQmax, kQmax);
         } else {
             return make_uint4(0u, 0u, 0u, 0u);
         }

@@ -104,3 +104,37 @@ def test_subnormal_scales_where_the_clamp_binds(oracle_lib, fmt, block):
     wg, vg = o_ring(w0, v0, x1, block)
     assert_same_codes(_bytes(gc), wg.view(np.uint8), "ring codes")
     assert_same_f32(to_host(gs), vg, "ring scales")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["int8", "e4m3", "int4"])
+def test_fast_path_quotients_just_above_q(oracle_lib, fmt, dtype):
+    """Normal block scales whose absmax element has a rounded quotient just
+    above Q (fl(m / fl(m / Q)) = the next binary32 value after Q): the fast
+    path takes no clamp, so the rounding to an integer (int8, 4-bit) or the
+    E4M3 conversion (448 + 2^-15 must give 448) has to land on Q.  Blocks
+    are picked from seeded absmax values by that property and checked
+    against the oracle."""
+    from block_wise_int8_amd import synth
+    block = 64
+    rng = np.random.default_rng(7)
+    m = (rng.uniform(1, 2, 400_000) * np.exp2(rng.integers(-80, 120, 400_000))).astype(np.float32)
+    if dtype == "bf16":
+        m = (m.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    q = np.float32(Q[fmt])
+    hit = m[(m / (m / q)) > q][:96]
+    assert hit.size == 96
+    x = (rng.uniform(-1, 1, (hit.size, block)) * hit[:, None]).astype(np.float32)
+    pos = rng.integers(0, block, hit.size)
+    x[np.arange(hit.size), pos] = np.where(rng.random(hit.size) < 0.5, hit, -hit)
+    x = x.reshape(-1)
+    if dtype == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+    quantize = CALLS[fmt][0]
+    o_quantize = _oracle(oracle_lib, fmt)[0]
+    say(f"fast-path quotient above Q: {fmt} {dtype}")
+    c, s = quantize(to_dev(x), block)
+    torch.cuda.synchronize()
+    wc, ws = o_quantize(x, block)
+    assert_same_codes(_bytes(c), wc.view(np.uint8), "codes")
+    assert_same_f32(to_host(s), ws, "scales")

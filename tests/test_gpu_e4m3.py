@@ -1,7 +1,8 @@
 """The FP8 E4M3 calls against the CPU oracle, element by element, through
 the C ABI: codes (bytes), scales and dequantized values bit for bit.
 
-The hardware conversion (v_cvt_pk_fp8_f32 after a clamp to +-448) is
+The hardware conversion (v_cvt_pk_fp8_f32; a clamp to +-448 first on the
+IEEE-division path, scales below 2^-90) is
 checked at every rounding boundary of the format: for scales that are powers
 of two the quotient is exact, so blocks can place it on every midpoint
 between neighbouring E4M3 values, one ulp either side, and on the values
