@@ -1,25 +1,26 @@
 """Benchmark of one GPU's share of the dynamic block-wise int8 quantized
-AllReduce (EQuARX) on the outlier workload: N=8 ranks x 16,777,216 bf16
-elements ~ N(0,1) with 0.1% N(0,1)*50 outliers, blocks of 256.
+AllReduce (EQuARX).
 
-One step = the whole per-GPU path over one batch, in one kernel
-(qar_quantize_reduce): quantize this GPU's own bf16 buffer (absmax -> scale
--> int8 codes, written out for the peers), dequantize it and the N-1 peers'
-quantized contributions (resident in HBM), fp32 sum in rank order,
-requantize, and dequantize the result back to bf16.  The peers' codes are
-produced by the quantize kernel before timing.  The same step as two
-kernels (quantize, then the plain reduce) is reported beside it.
-Buffer sets rotate every step (footprint > 1 GiB) so the 256 MB Infinity
-Cache cannot serve a step from the previous one's data: inputs are resident
-in HBM, not in cache, when a step starts.
+Headline (default): the small-block workload, N=16 ranks x 67,108,864 fp32
+elements ~ N(0, 1e-3) times a per-block LogNormal(0, 2) magnitude, blocks
+of 64.  One step = the one-shot fused reduce of the 16 quantized
+contributions (dequantize, fp32 sum in rank order, requantize; no
+dequantized output), pipelined as 8 chunks over 4 HIP streams (the caller's
+and 3 side streams, two chunks per stream) with
+qar_reduce_quantized_chunked.  The timed region forks the side streams off
+the caller's once, runs K independent steps over 2 rotated buffer sets
+(2.4 GB, far beyond the 256 MB Infinity Cache) and joins them once.
 
-Prints ONE JSON line.  value = bf16 payload bytes (N * n * 2) per step /
-step time.  roofline = the step's kernel against the
-MI355X HBM peak; cpu_baseline = the CPU oracle on the same inputs.
-Extra keys report each kernel's own time, the reduce without the fused
-dequantize (N*qbytes read + qbytes written) and a ring step.
+Prints ONE JSON line.  value = bf16-equivalent payload (N * n * 2 bytes)
+per step / step time (the fp32 payload rate beside it); roofline = the
+reduce kernel's algorithmic bytes per step over the step time against the
+MI355X HBM peak; cpu_baseline = the CPU oracle reducing the same inputs.
+Extra keys: the chunk/stream sweep, and the previous headline (the
+one-kernel step on the outlier workload, N=8 x 16,777,216 bf16, B=256)
+with its own extras (each kernel alone, the ring step, prefill, code
+formats, the one-GPU share, row-bounded blocks).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload smallblock|outliers]
 """
 from __future__ import annotations
 
@@ -65,13 +66,31 @@ def measured_traffic(workload_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counters_path_chunked(workload_key: str) -> str:
+    return os.path.join(PROFILES, f"{DOMINANT_CHUNKED}_{workload_key}_counters.json")
+
+
+def measured_traffic_chunked(workload_key: str):
+    """HBM bytes per step (all chunk launches) of the chunked headline step
+    from the committed counter summary, if taken on the current kernels."""
+    path = counters_path_chunked(workload_key)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=8, help="buffer sets rotated across steps")
-    p.add_argument("--workload", default="outliers")
+    p.add_argument("--workload", default="smallblock",
+                   help="smallblock (default: the chunked fused reduce) or a bf16 workload for the one-kernel step")
     p.add_argument("--skew", type=int, default=4096,
                    help="bytes added to the stride between rank code buffers in one allocation "
                         "(multiple of 16); -1 = one allocation per rank")
@@ -87,6 +106,8 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="instead of the step: the reduce (no output) and the one-kernel step over rank counts "
                         "and block sizes, one JSON line per point")
+    p.add_argument("--counter-run", action="store_true",
+                   help="only launch every hot-path kernel 4 times over rotated buffers (for rocprofv3 --pmc passes)")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="no GPU: read the rocprofv3 --pmc CSVs of the four counter passes under DIR "
                         "(pmc_copy_fetch, pmc_copy_write, pmc_fetch, pmc_write) and write the traffic summary "
@@ -94,55 +115,272 @@ def parse():
     return p.parse_args()
 
 
-# (name in the trace, algorithmic read bytes, algorithmic write bytes) for
-# the outlier workload's kernels; N ranks, n elements, block B, bf16 in/out
-def _counter_kernels(N, n, B):
-    qb = n + 4 * (n // B)
-    return [("k_quantize_reduce<256, 0, unsigned short, qar::Int8Codes, true>", 2 * n + (N - 1) * qb,
-             2 * qb + 2 * n),
-            ("k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", 2 * n, qb),
-            ("k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", N * qb, qb + 2 * n)]
+# ---------------------------------------------------------------------------
+# HBM traffic of every hot-path kernel: bench.py --counter-run launches each
+# kernel of the catalogue below 4 times (16 for the chunked step: 2 steps of
+# 8 chunks) over rotated buffer sets, so no launch finds its inputs in L2;
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes over that run, and over a
+# 1 GiB device copy for calibration, give each kernel's bytes per dispatch;
+# --summarize-counters writes the table under profiles/.
 
 
-def summarize_counters(d: str, out: str | None = None) -> int:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the step's kernels,
-    scaled by what the same counters read for a plain 1 GiB device copy;
-    written to `out` (default: the committed summary under profiles/)."""
+def counter_catalogue():
+    """(key, what, kernel name in the trace, grid threads, algorithmic read
+    bytes, algorithmic write bytes) per dispatch, for each kernel that
+    --counter-run launches.  Shapes are those of the workloads (the prefill
+    and small-block ones included); the grid is one 256-thread workgroup per
+    4,096 elements."""
+    from block_wise_int8_amd import synth
+
+    def grid(n):
+        return -(-n // 4096) * 256
+
+    def qb(n, B, per_byte=1):
+        return n // per_byte + 4 * (n // B)
+    W = synth.WORKLOADS
+    out = []
+    w5 = W["smallblock"]
+    n5c = w5.n // CHUNKS
+    out.append(("smallblock_reduce_chunk", f"small-block step: one of {CHUNKS} chunks of the fused reduce "
+                f"(N={w5.nranks} x {n5c:,} fp32-derived codes, B=64, no out)",
+                "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>", grid(n5c), w5.nranks * qb(n5c, 64),
+                qb(n5c, 64)))
+    out.append(("smallblock_quantize", f"small-block quantize (one rank: {w5.n:,} fp32, B=64)",
+                "k_quantize<64, float, qar::FlatLanes<64>, qar::Int8Codes>", grid(w5.n), 4 * w5.n, qb(w5.n, 64)))
+    w2 = W["outliers"]
+    N2, n2 = w2.nranks, w2.n
+    out.append(("outliers_step", f"outlier one-kernel step (N={N2} x {n2:,} bf16, B=256, own quantize + reduce "
+                f"+ bf16 out)", "k_quantize_reduce<256, 0, unsigned short, qar::Int8Codes, true>", grid(n2),
+                2 * n2 + (N2 - 1) * qb(n2, 256), 2 * qb(n2, 256) + 2 * n2))
+    out.append(("outliers_quantize", f"outlier quantize (one rank: {n2:,} bf16, B=256)",
+                "k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", grid(n2), 2 * n2,
+                qb(n2, 256)))
+    out.append(("outliers_reduce", f"outlier fused reduce, no out (N={N2})",
+                "k_reduce<256, -1, qar::FlatLanes<256>, qar::Int8Codes>", grid(n2), N2 * qb(n2, 256), qb(n2, 256)))
+    out.append(("outliers_reduce_bf16", f"outlier fused reduce + bf16 out (N={N2})",
+                "k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", grid(n2), N2 * qb(n2, 256),
+                qb(n2, 256) + 2 * n2))
+    out.append(("outliers_dequantize", "outlier dequantize to bf16",
+                "k_dequantize<256, unsigned short, qar::Int8Codes>", grid(n2), qb(n2, 256), 2 * n2))
+    out.append(("outliers_comparator", f"unquantized bf16 comparator (N={N2})",
+                "k_reduce_unquantized<unsigned short>", grid(n2), 2 * N2 * n2, 2 * n2))
+    out.append(("outliers_reduce_e4m3", "outlier fused reduce, E4M3 codes, no out",
+                "k_reduce<256, -1, qar::FlatLanes<256>, qar::E4M3Codes>", grid(n2), N2 * qb(n2, 256), qb(n2, 256)))
+    out.append(("outliers_step_e4m3", "outlier one-kernel step, E4M3 codes",
+                "k_quantize_reduce<256, 0, unsigned short, qar::E4M3Codes, true>", grid(n2),
+                2 * n2 + (N2 - 1) * qb(n2, 256), 2 * qb(n2, 256) + 2 * n2))
+    out.append(("outliers_reduce_int4", "outlier fused reduce, 4-bit codes, no out",
+                "k_reduce<256, -1, qar::FlatLanes<256>, qar::Int4Codes>", grid(n2), N2 * qb(n2, 256, 2),
+                qb(n2, 256, 2)))
+    out.append(("outliers_step_int4", "outlier one-kernel step, 4-bit codes",
+                "k_quantize_reduce<256, 0, unsigned short, qar::Int4Codes, true>", grid(n2),
+                2 * n2 + (N2 - 1) * qb(n2, 256, 2), 2 * qb(n2, 256, 2) + 2 * n2))
+    w3 = W["prefill"]
+    out.append(("prefill_reduce", f"prefill fused reduce, no out (N={w3.nranks} x [8192, 5376] bf16)",
+                "k_reduce<256, -1, qar::FlatLanes<256>, qar::Int8Codes>", grid(w3.n), w3.nranks * qb(w3.n, 256),
+                qb(w3.n, 256)))
+    out.append(("prefill_reduce_bf16", "prefill fused reduce + bf16 out",
+                "k_reduce<256, 0, qar::FlatLanes<256>, qar::Int8Codes>", grid(w3.n), w3.nranks * qb(w3.n, 256),
+                qb(w3.n, 256) + 2 * w3.n))
+    w4 = W["ring"]
+    out.append(("ring_step", "ring step (codes + scales in, bf16 local [2048, 3840], B=256)",
+                "k_ring_step<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", grid(w4.n),
+                qb(w4.n, 256) + 2 * w4.n, qb(w4.n, 256)))
+    out.append(("ring_quantize", "ring quantize of rank 0 ([2048, 3840] bf16)",
+                "k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", grid(w4.n), 2 * w4.n,
+                qb(w4.n, 256)))
+    return out
+
+
+def counter_run(qar, torch, synth, dev) -> int:
+    """Launches every kernel of counter_catalogue() (inputs drawn on the GPU),
+    4 dispatches each over rotated buffer sets; prints one line per kernel."""
+    W = synth.WORKLOADS
+    reps = 4
+
+    def sets_of(make, k):
+        return [make() for _ in range(k)]
+
+    def say(key):
+        print(json.dumps({"counter_run": key}), flush=True)
+
+    # small-block workload: the chunked step (2 steps) and a quantize
+    w = W["smallblock"]
+    N, n, B = w.nranks, w.n, w.block
+    xs = [synth.device_rank(w, r, dev) for r in range(N)]
+    q = [qar.qar_quantize_blocks(x, B) for x in xs]
+    sts = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(STREAMS - 1)]
+    ss = sets_of(lambda: ([c.clone() for c, _ in q], [s_.clone() for _, s_ in q],
+                          torch.empty(n, dtype=torch.int8, device=dev),
+                          torch.empty(n // B, dtype=torch.float32, device=dev)), 2)
+    del q
+    torch.cuda.synchronize()
+    say("smallblock_reduce_chunk")
+    for i in range(2):
+        c, s_, co, so = ss[i]
+        qar.qar_reduce_quantized_chunked(c, s_, B, CHUNKS, sts[:1], co, so)
+    torch.cuda.synchronize()
+    del ss
+    say("smallblock_quantize")
+    for i in range(reps):
+        qar.qar_quantize_blocks(xs[i], B)
+    torch.cuda.synchronize()
+    del xs
+    torch.cuda.empty_cache()
+
+    # outlier workload: int8, E4M3 and 4-bit kernels, comparator
+    w = W["outliers"]
+    N, n, B = w.nranks, w.n, w.block
+    xs = [synth.device_rank(w, r, dev) for r in range(N)]
+    fmts = {"": (qar.qar_quantize_blocks, qar.qar_reduce_quantized, qar.qar_quantize_reduce, 1),
+            "_e4m3": (qar.qar_quantize_blocks_e4m3, qar.qar_reduce_quantized_e4m3, qar.qar_quantize_reduce_e4m3, 1),
+            "_int4": (qar.qar_quantize_blocks_int4, qar.qar_reduce_quantized_int4, qar.qar_quantize_reduce_int4, 2)}
+    for sfx, (quant, red, qred, per_byte) in fmts.items():
+        q = [quant(x, B) for x in xs]
+        ss = sets_of(lambda: ([c.clone() for c, _ in q], [s_.clone() for _, s_ in q],
+                              torch.empty(n // per_byte, dtype=q[0][0].dtype, device=dev),
+                              torch.empty(n // B, dtype=torch.float32, device=dev),
+                              torch.empty(n, dtype=torch.bfloat16, device=dev), xs[0].clone()), reps)
+        del q
+        torch.cuda.synchronize()
+        tag = sfx.replace("_", "") or "int8"
+        say(f"outliers_step ({tag})")
+        for c, s_, co, so, out, x in ss:
+            qred(x, 0, c, s_, B, co, so, out=out)
+        torch.cuda.synchronize()
+        say(f"outliers_reduce ({tag})")
+        for c, s_, co, so, out, x in ss:
+            red(c, s_, B, co, so)
+        torch.cuda.synchronize()
+        if not sfx:
+            say("outliers_reduce_bf16")
+            for c, s_, co, so, out, x in ss:
+                red(c, s_, B, co, so, out=out)
+            torch.cuda.synchronize()
+            say("outliers_quantize")
+            for c, s_, co, so, out, x in ss:
+                quant(x, B, c[0], s_[0])
+            torch.cuda.synchronize()
+            say("outliers_dequantize")
+            for c, s_, co, so, out, x in ss:
+                qar.qar_dequantize(c[1], s_[1], B, out=out)
+            torch.cuda.synchronize()
+        del ss
+        torch.cuda.empty_cache()
+    say("outliers_comparator")
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    cmp_sets = [[x.clone() for x in xs] for _ in range(2)]
+    for i in range(reps):
+        qar.qar_reduce_unquantized(cmp_sets[i % 2], out=outs[i % 2])
+    torch.cuda.synchronize()
+    del xs, outs, cmp_sets
+    torch.cuda.empty_cache()
+
+    # prefill workload: the fused reduce without and with bf16 out
+    w = W["prefill"]
+    N, n, B = w.nranks, w.n, w.block
+    q = []
+    for r in range(N):
+        q.append(qar.qar_quantize_blocks(synth.device_rank(w, r, dev), B))
+    ss = sets_of(lambda: ([c.clone() for c, _ in q], [s_.clone() for _, s_ in q],
+                          torch.empty(n, dtype=torch.int8, device=dev),
+                          torch.empty(n // B, dtype=torch.float32, device=dev),
+                          torch.empty(n, dtype=torch.bfloat16, device=dev)), 2)
+    del q
+    torch.cuda.synchronize()
+    say("prefill_reduce")
+    for i in range(reps):
+        c, s_, co, so, out = ss[i % 2]
+        qar.qar_reduce_quantized(c, s_, B, co, so)
+    torch.cuda.synchronize()
+    say("prefill_reduce_bf16")
+    for i in range(reps):
+        c, s_, co, so, out = ss[i % 2]
+        qar.qar_reduce_quantized(c, s_, B, co, so, out=out)
+    torch.cuda.synchronize()
+    del ss
+    torch.cuda.empty_cache()
+
+    # ring workload: quantize of rank 0 and a ring step, 8 sets (254 MB)
+    w = W["ring"]
+    n, B = w.n, w.block
+    x0, x1 = synth.device_rank(w, 0, dev), synth.device_rank(w, 1, dev)
+    c0, s0 = qar.qar_quantize_blocks(x0, B)
+    ss = sets_of(lambda: (x0.clone(), c0.clone(), s0.clone(), x1.clone(), torch.empty_like(c0),
+                          torch.empty_like(s0)), 8)
+    torch.cuda.synchronize()
+    say("ring_step")
+    for x, c, s_, loc, co, so in ss[:reps]:
+        qar.qar_ring_step(c, s_, loc, B, co, so)
+    torch.cuda.synchronize()
+    say("ring_quantize")
+    for x, c, s_, loc, co, so in ss[reps:]:
+        qar.qar_quantize_blocks(x, B, c, s_)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": "done", "catalogue": [e[0] for e in counter_catalogue()]}), flush=True)
+    return 0
+
+
+def summarize_counters(d: str, out_dir: str = PROFILES) -> int:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every catalogue kernel
+    from the four passes' CSVs under d (pmc_copy_fetch, pmc_copy_write:
+    a 1 GiB device copy; pmc_fetch, pmc_write: --counter-run), scaled by
+    what the same counters read for the copy; writes the table and its JSON
+    under profiles/, plus the per-launch figures bench.py reads for the two
+    headline kernels."""
     import csv
     import statistics
 
-    def mean_kib(sub, match):
+    def rows_of(sub):
         files = [os.path.join(r, f) for r, _, fs in os.walk(os.path.join(d, sub)) for f in fs
                  if f.endswith("counter_collection.csv")]
-        v = [float(r["Counter_Value"]) for p in files for r in csv.DictReader(open(p)) if match in r["Kernel_Name"]]
-        if not v:
-            raise SystemExit(f"no dispatch of {match} under {d}/{sub}")
-        return statistics.mean(v), len(v)
+        rows = [r for p in files for r in csv.DictReader(open(p))]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        if not rows:
+            raise SystemExit(f"no counter rows under {d}/{sub}")
+        return rows
+
+    def mean_kib(rows, name, grid, last):
+        v = [float(r["Counter_Value"]) for r in rows if name in r["Kernel_Name"] and int(r["Grid_Size"]) == grid]
+        if len(v) < last:
+            raise SystemExit(f"{len(v)} dispatches of {name} with grid {grid}, expected at least {last}")
+        return statistics.mean(v[-last:])
 
     copy_kib = 1 << 20
-    cf, _ = mean_kib("pmc_copy_fetch", "copyBuffer")
-    cw, _ = mean_kib("pmc_copy_write", "copyBuffer")
+    crf = [float(r["Counter_Value"]) for r in rows_of("pmc_copy_fetch") if "copyBuffer" in r["Kernel_Name"]]
+    crw = [float(r["Counter_Value"]) for r in rows_of("pmc_copy_write") if "copyBuffer" in r["Kernel_Name"]]
+    cf, cw = statistics.mean(crf), statistics.mean(crw)
     ff, fw = copy_kib / cf, copy_kib / cw
-    from block_wise_int8_amd import synth
-    w = synth.WORKLOADS["outliers"]
-    rows = {}
-    for name, alg_r, alg_w in _counter_kernels(w.nranks, w.n, w.block):
-        f, nd = mean_kib("pmc_fetch", name)
-        wr, _ = mean_kib("pmc_write", name)
+    fetch, write = rows_of("pmc_fetch"), rows_of("pmc_write")
+    kernels = {}
+    for key, what, name, grid, alg_r, alg_w in counter_catalogue():
+        last = 2 * CHUNKS if key == "smallblock_reduce_chunk" else 4
+        f = mean_kib(fetch, name, grid, last)
+        wr = mean_kib(write, name, grid, last)
         rd, wb = int(f * ff * 1024), int(wr * fw * 1024)
-        rows[name.split("<")[0]] = {"dispatches": nd, "fetch_kib_raw_mean": round(f, 2), "write_kib_raw_mean": round(wr, 2),
-                                  "hbm_read_bytes": rd, "hbm_write_bytes": wb, "algorithmic_read_bytes": alg_r,
-                                  "algorithmic_write_bytes": alg_w,
-                                  "traffic_over_algorithmic": round((rd + wb) / (alg_r + alg_w), 4)}
-    top = rows[DOMINANT]
-    rec = {"kernel": DOMINANT, "workload": f"{w.key}: {w.description}",
-           "kernel_source_sha256_16": kernel_source_hash(),
-           "calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": round(cf, 2), "write_kib_raw": round(cw, 2),
-                           "fetch_factor": round(ff, 5), "write_factor": round(fw, 5)},
-           "hbm_bytes_per_launch": top["hbm_read_bytes"] + top["hbm_write_bytes"],
-           "kernels": rows}
-    with open(out or counters_path(w.key), "w") as f:
+        kernels[key] = {"what": what, "kernel": name, "grid_threads": grid, "dispatches": last,
+                        "fetch_kib_raw_mean": round(f, 2), "write_kib_raw_mean": round(wr, 2),
+                        "hbm_read_bytes": rd, "hbm_write_bytes": wb, "algorithmic_read_bytes": alg_r,
+                        "algorithmic_write_bytes": alg_w,
+                        "traffic_over_algorithmic": round((rd + wb) / (alg_r + alg_w), 4)}
+    sha = kernel_source_hash()
+    calib = {"copy_bytes": copy_kib * 1024, "fetch_kib_raw": round(cf, 2), "write_kib_raw": round(cw, 2),
+             "fetch_factor": round(ff, 5), "write_factor": round(fw, 5), "copy_dispatches": len(crf)}
+    rec = {"kernel_source_sha256_16": sha, "calibration": calib, "kernels": kernels}
+    with open(os.path.join(out_dir, "hbm_traffic_all_kernels.json"), "w") as f:
         json.dump(rec, f, indent=1)
+    k5 = kernels["smallblock_reduce_chunk"]
+    with open(os.path.join(out_dir, os.path.basename(counters_path_chunked("smallblock"))), "w") as f:
+        json.dump({"kernel": DOMINANT_CHUNKED, "workload": k5["what"], "kernel_source_sha256_16": sha,
+                   "calibration": calib, "launches_per_step": CHUNKS,
+                   "hbm_bytes_per_launch": k5["hbm_read_bytes"] + k5["hbm_write_bytes"],
+                   "hbm_bytes_per_step": CHUNKS * (k5["hbm_read_bytes"] + k5["hbm_write_bytes"]),
+                   "traffic_over_algorithmic": k5["traffic_over_algorithmic"]}, f, indent=1)
+    k2 = kernels["outliers_step"]
+    with open(os.path.join(out_dir, os.path.basename(counters_path("outliers"))), "w") as f:
+        json.dump({"kernel": DOMINANT, "workload": k2["what"], "kernel_source_sha256_16": sha,
+                   "calibration": calib, "hbm_bytes_per_launch": k2["hbm_read_bytes"] + k2["hbm_write_bytes"],
+                   "traffic_over_algorithmic": k2["traffic_over_algorithmic"]}, f, indent=1)
     print(json.dumps(rec, indent=1))
     return 0
 
@@ -171,6 +409,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.sweep:
         return sweep(qar, torch, synth, dev, args.skew)
+    if args.counter_run:
+        return counter_run(qar, torch, synth, dev)
     if args.copy_probe_mib:
         # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of these
         # dispatches calibrate the counters (bytes read = bytes written =
@@ -183,7 +423,20 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": nbytes, "launches": 8}))
         return 0
-    w = synth.WORKLOADS[args.workload]
+    if args.workload == "smallblock":
+        result = smallblock_headline(args, qar, torch, np, synth, dev)
+    else:
+        result = outlier_headline(args, qar, torch, np, synth, dev, args.workload)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def outlier_headline(args, qar, torch, np, synth, dev, workload, as_extra=False):
+    """The one-kernel step (quantize own + reduce + dequantize) on a bf16
+    workload (default: the outlier workload) with its own extras; the whole
+    record when it is the headline, its step figures and the extras when
+    as_extra."""
+    w = synth.WORKLOADS[workload]
     N, n, B = w.nranks, w.n, w.block
     nb = n // B
     qbytes = n + 4 * nb
@@ -372,18 +625,292 @@ def main() -> int:
         result["copy_reference"]["copy_time_over_step_time"] = round(result["copy_reference"]["avg_us"] / f_us, 4)
         result["ring_step"] = ring_bench(qar, torch, np, synth, dev)
         result["prefill"] = prefill_bench(qar, torch, synth, dev, args.skew)
-        result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
+        if not as_extra:
+            result["smallblock_pipelined"] = pipelined_bench(qar, torch, synth, dev, args.skew)
         result["allreduce_simulated"] = allreduce_bench(qar, torch, synth, dev)
         result["code_formats"] = code_formats_bench(qar, torch, synth, dev, args.skew)
         result["tiny"] = tiny_bench(qar, torch, synth, dev)
         result["one_gpu_share"] = share_bench(qar, torch, synth, dev, args.skew)
         result["row_bounded"] = rows_bench(qar, torch, dev)
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not as_extra:
         result["cpu_baseline"] = cpu_baseline(args, np, w, host, sets[0], torch)
 
-    print(json.dumps(result), flush=True)
-    return 0
+    return result
+
+
+# The headline step on the small-block workload: the fused reduce cut into
+# CHUNKS block-aligned chunks over STREAMS streams (the caller's stream and
+# STREAMS - 1 side streams), two chunks per stream per step.
+CHUNKS, STREAMS = 8, 4
+DOMINANT_CHUNKED = "k_reduce"
+
+
+def smallblock_headline(args, qar, torch, np, synth, dev):
+    """N=16 ranks x 67,108,864 fp32 elements, block 64: the one-shot fused
+    reduce (dequantize the 16 quantized contributions, fp32 sum in rank
+    order, requantize; no dequantized output), each step one
+    qar_reduce_quantized_chunked call: 8 chunks of 8,388,608 elements, chunk
+    c on stream c % 4, so every stream holds two chunks of a step and the
+    next step's queue behind them.  Steps rotate over 2 buffer sets (2.4 GB,
+    far beyond the 256 MB Infinity Cache).  The timed region forks the 4
+    streams off the caller's stream once, runs K steps, and joins them once;
+    the steps are independent (rotated buffers), so one step's drain
+    overlaps the next one's ramp on other streams.
+
+    Inputs: the recipe drawn on the GPU (synth.device_rank: torch's
+    generator), copied to the host for the CPU oracle, which quantizes and
+    reduces them on its own."""
+    w = synth.WORKLOADS["smallblock"]
+    N, n, B = w.nranks, w.n, w.block
+    nb = n // B
+    qbytes = n + 4 * nb
+    main_st = torch.cuda.Stream()
+    sides = [torch.cuda.Stream() for _ in range(STREAMS - 1)]
+    streams = [main_st] + sides
+    t0 = time.time()
+    with torch.cuda.stream(main_st):
+        xs = [synth.device_rank(w, r, dev) for r in range(N)]
+        codes, scales = [], []
+        for x in xs:
+            c, s_ = qar.qar_quantize_blocks(x, B, stream=main_st)
+            codes.append(c), scales.append(s_)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    host_x = [x.cpu().numpy() for x in xs] if not args.no_cpu_baseline else None
+    input_sha = [synth.sha256(h)[:16] for h in host_x] if host_x is not None else None
+    del xs
+    nsets = 2                                   # 2 x 1.21 GB
+    sets = []
+    with torch.cuda.stream(main_st):
+        for _ in range(nsets):
+            sets.append({"codes": _rank_block(torch, codes, args.skew, dev), "scales": [x.clone() for x in scales],
+                         "co": torch.empty(n, dtype=torch.int8, device=dev),
+                         "so": torch.empty(nb, dtype=torch.float32, device=dev)})
+    torch.cuda.synchronize()
+    del codes, scales
+    torch.cuda.empty_cache()
+
+    def step(i):
+        st = sets[i % nsets]
+        qar.qar_reduce_quantized_chunked(st["codes"], st["scales"], B, CHUNKS, streams, st["co"], st["so"])
+
+    def fork():
+        ev = torch.cuda.Event()
+        ev.record(main_st)
+        for s_ in sides:
+            s_.wait_event(ev)
+
+    def join():
+        for s_ in sides:
+            ev = torch.cuda.Event()
+            ev.record(s_)
+            main_st.wait_event(ev)
+
+    with torch.cuda.stream(main_st):
+        # preheat (the chip's clock transient after idle), then W warm-up
+        # steps, then the timed region, each between one fork and one join
+        fork()
+        for i in range(3):
+            step(i)
+        join()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main_st)
+        fork()
+        for i in range(8):
+            step(i)
+        join()
+        b.record(main_st)
+        torch.cuda.synchronize()
+        est_us = a.elapsed_time(b) * 1e3 / 8
+        pre = min(int(PREHEAT_MS * 1e3 / est_us) + 1, 5000) if PREHEAT_MS > 0 else 0
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        fork()
+        for i in range(pre + args.warmup):
+            step(i)
+        join()
+        t_start.record(main_st)
+        fork()
+        for i in range(args.steps):
+            step(pre + args.warmup + i)
+        join()
+        t_end.record(main_st)
+        torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    step_us = ms_per_step * 1e3
+    step_bytes = (N + 1) * qbytes
+    payload_bf16 = N * n * 2
+    achieved = step_bytes / (step_us * 1e-6) / 1e9
+
+    result = {
+        "metric": "GB/s of bf16 payload reduced per GPU and % of HBM peak, fused quantized reduce",
+        "value": round(payload_bf16 / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key}: {w.description}",
+            "nranks": N, "elements_per_rank": n, "block": B, "input_dtype": w.dtype,
+            "seed": w.seed, "input_recipe": "synth.device_rank (torch's generator on the GPU, seeded)",
+            "input_sha256_16": input_sha,
+            "step": (f"one-shot fused reduce (dequantize {N} quantized contributions, fp32 sum in rank order, "
+                     f"requantize; no dequantized output) as one qar_reduce_quantized_chunked call: {CHUNKS} "
+                     f"chunks over {STREAMS} streams (the caller's + {STREAMS - 1}), two chunks per stream"),
+            "codes": f"int8 with one fp32 scale per block of {B} (arithmetic in fp32)",
+            "payload": "bf16-equivalent: N * n * 2 bytes per step (the inputs are fp32; fp32 payload beside it)",
+            "buffer_sets": nsets, "footprint_bytes": nsets * (N + 1) * qbytes,
+            "parallelism": "one GPU's share",
+        },
+        "payload_fp32_GBps": round(N * n * 4 / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": DOMINANT_CHUNKED,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic_chunked(w.key),
+            "algorithmic_bytes_per_step": step_bytes,
+            "launches_per_step": CHUNKS,
+            "algorithmic_bytes_per_launch": step_bytes // CHUNKS,
+            "step_us": round(step_us, 3),
+            "timing": (f"{args.steps} steps between two HIP events on the caller's stream, which forks the "
+                       f"{STREAMS - 1} side streams once before the steps and joins them once after; behind "
+                       f"{pre} preheat and {args.warmup} warm-up steps.  A step's {CHUNKS} launches run "
+                       f"concurrently on {STREAMS} streams, so the kernel's rate is the step's bytes over the "
+                       f"step's time"),
+        },
+        "timed_region": {"preheat_steps": pre, "warmup_steps": args.warmup, "steps": args.steps},
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not args.no_extras:
+        result["chunk_sweep"] = chunk_sweep(qar, torch, sets, B, N, n, qbytes, main_st, sides)
+    if host_x is not None:
+        gpu_c, gpu_s = sets[0]["co"].cpu().numpy(), sets[0]["so"].cpu().numpy()
+        del sets
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline_reduce(args, np, w, host_x, gpu_c, gpu_s)
+        del host_x
+    else:
+        del sets
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        out = outlier_headline(args, qar, torch, np, synth, dev, "outliers", as_extra=True)
+        result["outliers_step"] = {k: out[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                                       "kernels", "two_kernel_step")}
+        for k, v in out.items():
+            if k not in result and k not in _HEADLINE_KEYS:
+                result[k] = v
+    return result
+
+
+_HEADLINE_KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                  "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "timed_region",
+                  "input_generation_s", "kernels", "two_kernel_step"}
+
+
+def chunk_sweep(qar, torch, sets, B, N, n, qbytes, main_st, sides):
+    """The same reduce on the same sets: one launch per step; chunked over
+    streams with one fork/join per timed segment (as the headline); and the
+    fork/join-per-call qar_reduce_quantized_pipelined, eager and as HIP
+    graph replays.  Bit-identical results in every row."""
+    nbytes = (N + 1) * qbytes
+    nsets = len(sets)
+    rows = []
+
+    def fork(strs):
+        ev = torch.cuda.Event()
+        ev.record(main_st)
+        for s_ in strs:
+            if s_ is not main_st:
+                s_.wait_event(ev)
+
+    def join(strs):
+        for s_ in strs:
+            if s_ is not main_st:
+                ev = torch.cuda.Event()
+                ev.record(s_)
+                main_st.wait_event(ev)
+
+    def seg_timed(fn, strs, reps=40):
+        with torch.cuda.stream(main_st):
+            fork(strs)
+            for i in range(3):
+                fn(i)
+            join(strs)
+            torch.cuda.synchronize()
+            pre = int(PREHEAT_MS * 1e3 / 200) + 1 if PREHEAT_MS > 0 else 0
+            fork(strs)
+            for i in range(pre):
+                fn(i)
+            join(strs)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[0].record(main_st)
+            per, j = reps // 5, 0
+            for k in range(5):
+                fork(strs)
+                for _ in range(per):
+                    fn(j)
+                    j += 1
+                join(strs)
+                ev[k + 1].record(main_st)
+            torch.cuda.synchronize()
+        seg = sorted(ev[k].elapsed_time(ev[k + 1]) / per * 1e3 for k in range(5))
+        return seg[2], seg[0]
+
+    def single(i):
+        st = sets[i % nsets]
+        qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["co"], st["so"], stream=main_st)
+    r = _rate(nbytes, seg_timed(single, [main_st]))
+    r.update({"call": "qar_reduce_quantized", "nchunks": 1, "nstreams": 1})
+    rows.append(r)
+    for nchunks, strs, tag in ((8, [main_st] + sides, "caller + 3 side streams"),
+                               (4, [main_st] + sides, "caller + 3 side streams"),
+                               (16, [main_st] + sides, "caller + 3 side streams"),
+                               (4, sides[:2], "2 side streams"),
+                               (2, sides[:2], "2 side streams")):
+        def fn(i, nchunks=nchunks, strs=strs):
+            st = sets[i % nsets]
+            qar.qar_reduce_quantized_chunked(st["codes"], st["scales"], B, nchunks, strs, st["co"], st["so"])
+        r = _rate(nbytes, seg_timed(fn, strs))
+        r.update({"call": "qar_reduce_quantized_chunked", "nchunks": nchunks, "nstreams": len(strs),
+                  "streams": tag})
+        rows.append(r)
+    for nchunks in (4, 8):
+        def fp(i, nchunks=nchunks):
+            st = sets[i % nsets]
+            qar.qar_reduce_quantized_pipelined(st["codes"], st["scales"], B, nchunks, [main_st] + sides, st["co"],
+                                               st["so"], stream=main_st)
+        r = _rate(nbytes, seg_timed(fp, [main_st], reps=20))
+        r.update({"call": "qar_reduce_quantized_pipelined (fork and join in every call)", "nchunks": nchunks,
+                  "nstreams": STREAMS})
+        rows.append(r)
+        with torch.cuda.stream(main_st):
+            fp(0), fp(1)
+            torch.cuda.synchronize()
+            graphs = []
+            for i in range(nsets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=main_st):
+                    fp(i)
+                graphs.append(g)
+            torch.cuda.synchronize()
+        r = _rate(nbytes, seg_timed(lambda i: graphs[i % nsets].replay(), [main_st], reps=20))
+        r.update({"call": "qar_reduce_quantized_pipelined, HIP graph replay", "nchunks": nchunks,
+                  "nstreams": STREAMS})
+        rows.append(r)
+        del graphs
+    return {"rows": rows, "note": "median (and fastest) of 5 event-bracketed segments per row; chunked rows fork "
+                                  "and join their streams once per segment"}
 
 
 def sweep(qar, torch, synth, dev, skew) -> int:
@@ -1005,6 +1532,68 @@ def copy_reference(torch, nbytes, dev):
     r = _rate(2 * half, _loop_us(torch, fn, len(pairs), 100, with_min=True))
     r["what"] = f"torch copy_ (the runtime's blit kernel) of {half:,} bytes, 8 rotated buffer pairs"
     return r
+
+
+def cpu_baseline_reduce(args, np, w, host_x, gpu_codes, gpu_scales):
+    """The CPU oracle (plain scalar C) running the headline step on the same
+    inputs: the one-shot reduce of the N ranks' quantized contributions
+    (codes and scales from the oracle's own quantize of the raw inputs,
+    untimed).  Timed on one host thread over the whole buffer, then on T
+    threads, each reducing its own block-aligned range with the same oracle
+    call (ctypes releases the GIL during the calls).  Also checks the GPU
+    step's codes and scales against the oracle's."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    o = oracle.load()
+    B, N, n = w.block, w.nranks, w.n
+    T = _cpu_threads()
+    with ThreadPoolExecutor(T) as pool:
+        qs = list(pool.map(lambda x: o.quantize(x, B), host_x))      # untimed
+    codes = [q[0] for q in qs]
+    scales = [q[1] for q in qs]
+    del qs
+
+    def part(lo, hi):
+        return o.reduce([c[lo:hi] for c in codes], [s_[lo // B:hi // B] for s_ in scales], B)
+
+    t0 = time.perf_counter()
+    oc, os_ = part(0, n)
+    dt1 = time.perf_counter() - t0
+    reps1 = max(1, int(args.cpu_seconds / 4 / dt1))
+    t0 = time.perf_counter()
+    for _ in range(reps1):
+        oc, os_ = part(0, n)
+    dt1 = (time.perf_counter() - t0) / reps1
+    nb = n // B
+    cuts = [(nb * k // T) * B for k in range(T + 1)]
+    with ThreadPoolExecutor(T) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda k: part(cuts[k], cuts[k + 1]), range(T)))           # warm the pool
+        reps = max(1, args.cpu_reps, int(args.cpu_seconds / (time.perf_counter() - t0)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            parts = list(pool.map(lambda k: part(cuts[k], cuts[k + 1]), range(T)))
+        dtT = (time.perf_counter() - t0) / reps
+    same_split = all(np.array_equal(p[0], oc[cuts[k]:cuts[k + 1]]) for k, p in enumerate(parts))
+    same = bool(np.array_equal(gpu_codes, oc)) and bool(np.array_equal(gpu_scales.view(np.uint32),
+                                                                         os_.view(np.uint32)))
+    payload = N * n * 2
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(payload / dtT / 1e9, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "cpu_model": model,
+            "sample": f"the whole workload: {reps} repetitions of the step (the one-shot reduce of {N} ranks x "
+                      f"{n:,} elements, block {B}) on {T} host threads, each on its own block range; "
+                      f"{dtT:.3f} s per step; GB/s of bf16-equivalent payload, as the headline",
+            "single_thread": {"value": round(payload / dt1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "seconds_per_step": round(dt1, 4), "repetitions": reps1},
+            "threads_agree_with_single_thread": bool(same_split),
+            "gpu_output_matches_oracle": same}
 
 
 def _cpu_threads() -> int:

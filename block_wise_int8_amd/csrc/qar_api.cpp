@@ -8,6 +8,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "qar_launch.h"
 
 static_assert(QAR_MAX_RANKS == qar::kMaxRanks, "rank limit mismatch");
@@ -98,36 +101,93 @@ void fill_ranks(qar::RankPtrs& rp, const int8_t* const* codes, const float* cons
     }
 }
 
-// The pipelined call's events, created once per thread and device and then
-// reused.  Re-recording an event does not disturb waits already enqueued on
-// its previous record, so consecutive calls may share them.  They are never
-// destroyed (a handful per thread and device, released with the process).
+// HIP events of the calls that fork work onto side streams and join it back
+// (timing disabled).  A call takes one set from its device's pool while it
+// enqueues and gives it back before returning: re-recording an event does not
+// disturb waits already enqueued on its previous record, so a set can serve
+// the next call at once.  Sets are created on demand and kept for the life of
+// the process, one per call in flight at the same time on a device (not one
+// per thread).
 constexpr int kEventDevices = 64;
 struct EventSet {
-    bool made;
-    hipEvent_t ev[1 + QAR_MAX_STREAMS];
+    hipEvent_t ev[1 + QAR_MAX_STREAMS]; // ev[0]: fork, ev[1 + i]: side stream i done
 };
-thread_local EventSet g_events[kEventDevices];
+std::mutex g_event_mu;
+std::vector<EventSet*> g_event_pool[kEventDevices];
 
-hipError_t pipeline_events(hipEvent_t** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kEventDevices) return hipErrorInvalidDevice;
-    EventSet& set = g_events[dev];
-    if (!set.made) {
+class PooledEvents {
+  public:
+    hipError_t acquire() {
+        hipError_t e = hipGetDevice(&dev_);
+        if (e != hipSuccess) return e;
+        if (dev_ < 0 || dev_ >= kEventDevices) return hipErrorInvalidDevice;
+        {
+            std::lock_guard<std::mutex> lock(g_event_mu);
+            if (!g_event_pool[dev_].empty()) {
+                set_ = g_event_pool[dev_].back();
+                g_event_pool[dev_].pop_back();
+                return hipSuccess;
+            }
+        }
+        EventSet* fresh = new EventSet;
         for (int i = 0; i < 1 + QAR_MAX_STREAMS; ++i) {
-            e = hipEventCreateWithFlags(&set.ev[i], hipEventDisableTiming);
+            e = hipEventCreateWithFlags(&fresh->ev[i], hipEventDisableTiming);
             if (e != hipSuccess) {
-                for (int j = 0; j < i; ++j) (void)hipEventDestroy(set.ev[j]);
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(fresh->ev[j]);
+                delete fresh;
                 return e;
             }
         }
-        set.made = true;
+        set_ = fresh;
+        return hipSuccess;
     }
-    *out = set.ev;
-    return hipSuccess;
-}
+    hipEvent_t* ev() const { return set_->ev; }
+    ~PooledEvents() {
+        if (!set_) return;
+        std::lock_guard<std::mutex> lock(g_event_mu);
+        g_event_pool[dev_].push_back(set_);
+    }
+
+  private:
+    int dev_ = 0;
+    EventSet* set_ = nullptr;
+};
+
+// Work on streams[0 .. used-1] starts after everything already enqueued on
+// `main` and `main` waits for all of it.  A side stream that is `main` itself
+// needs neither, so a call whose only stream is `main` records no event.
+class ForkJoin {
+  public:
+    ForkJoin(hipStream_t main, void* const* streams, uint32_t used) : main_(main), streams_(streams), used_(used) {
+        for (uint32_t i = 0; i < used; ++i) any_side_ |= (hipStream_t)streams[i] != main;
+    }
+    hipError_t fork() {
+        if (!any_side_) return hipSuccess;
+        hipError_t e = events_.acquire();
+        if (e == hipSuccess) e = hipEventRecord(events_.ev()[0], main_);
+        for (uint32_t i = 0; e == hipSuccess && i < used_; ++i)
+            if (is_side(i)) e = hipStreamWaitEvent(stream(i), events_.ev()[0], 0);
+        return e;
+    }
+    hipError_t join() {
+        hipError_t e = hipSuccess;
+        for (uint32_t i = 0; any_side_ && e == hipSuccess && i < used_; ++i) {
+            if (!is_side(i)) continue;
+            e = hipEventRecord(events_.ev()[1 + i], stream(i));
+            if (e == hipSuccess) e = hipStreamWaitEvent(main_, events_.ev()[1 + i], 0);
+        }
+        return e;
+    }
+
+  private:
+    hipStream_t stream(uint32_t i) const { return (hipStream_t)streams_[i]; }
+    bool is_side(uint32_t i) const { return stream(i) != main_; }
+    hipStream_t main_;
+    void* const* streams_;
+    uint32_t used_;
+    bool any_side_ = false;
+    PooledEvents events_;
+};
 
 int out_kind(const void* out, qar_dtype d) {
     if (!out) return qar::kOutNone;
@@ -283,6 +343,58 @@ qar_status qar_quantize_reduce_int4(const void* x_own, qar_dtype dtype, uint32_t
                                 "qar_quantize_reduce_int4");
 }
 
+} // extern "C"
+
+namespace {
+
+// Chunk c of the reduce (block-aligned, equal but for the last) on
+// streams[c % used], each behind whatever its stream already holds.
+hipError_t chunks_run(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
+                      uint32_t block, int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
+                      uint32_t nchunks, void* const* streams, uint32_t used) {
+    const size_t nb = n / block;
+    const size_t chunks = nchunks < nb ? nchunks : nb;
+    const size_t per = (nb + chunks - 1) / chunks; // blocks per chunk
+    const int kind = out_kind(out, out_dtype);
+    const size_t out_bytes = out ? dtype_bytes(out_dtype) : 0;
+    hipError_t e = hipSuccess;
+    for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
+        const size_t b0 = c * per;
+        if (b0 >= nb) break;
+        const size_t bn = (nb - b0 < per) ? nb - b0 : per;
+        const size_t e0 = b0 * block;
+        qar::RankPtrs rp;
+        fill_ranks(rp, codes, scales, nranks, e0, b0);
+        void* out_c = out ? (void*)((char*)out + e0 * out_bytes) : nullptr;
+        e = qar::launch_reduce(rp, (int)nranks, bn * block, (int)block, codes_out + e0, scales_out + b0, out_c,
+                               kind, (hipStream_t)streams[c % used]);
+    }
+    return e;
+}
+
+uint32_t streams_used(uint32_t nchunks, size_t n, uint32_t block, uint32_t nstreams) {
+    const size_t nb = n / block;
+    const size_t chunks = nchunks < nb ? nchunks : nb;
+    return (uint32_t)(chunks < nstreams ? chunks : nstreams);
+}
+
+} // namespace
+
+extern "C" {
+
+qar_status qar_reduce_quantized_chunked(const int8_t* const* codes, const float* const* scales, uint32_t nranks,
+                                        size_t n, uint32_t block, int8_t* codes_out, float* scales_out, void* out,
+                                        qar_dtype out_dtype, uint32_t nchunks, void* const* streams,
+                                        uint32_t nstreams) {
+    if (n == 0) return QAR_OK;
+    qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
+    if (st != QAR_OK) return st;
+    if (nchunks == 0 || !streams || nstreams == 0 || nstreams > QAR_MAX_STREAMS) return QAR_ERR_INVALID_ARG;
+    const hipError_t e = chunks_run(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype, nchunks,
+                                    streams, streams_used(nchunks, n, block, nstreams));
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_chunked");
+}
+
 qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
                                           uint32_t nranks, size_t n, uint32_t block, int8_t* codes_out,
                                           float* scales_out, void* out, qar_dtype out_dtype,
@@ -292,38 +404,15 @@ qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const floa
     qar_status st = check_reduce(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype);
     if (st != QAR_OK) return st;
     if (nchunks == 0 || !streams || nstreams == 0 || nstreams > QAR_MAX_STREAMS) return QAR_ERR_INVALID_ARG;
+    // NULL (the default stream) only as the calling stream itself
     for (uint32_t i = 0; i < nstreams; ++i)
-        if (!streams[i]) return QAR_ERR_INVALID_ARG;
-
-    const size_t nb = n / block;
-    const size_t chunks = nchunks < nb ? nchunks : nb;
-    const size_t per = (nb + chunks - 1) / chunks; // blocks per chunk
-    const hipStream_t main_st = (hipStream_t)stream;
-    const int kind = out_kind(out, out_dtype);
-    const size_t out_bytes = out ? (out_dtype == QAR_BF16 ? 2 : 4) : 0;
-    const uint32_t used = (uint32_t)(chunks < nstreams ? chunks : nstreams);
-
-    hipEvent_t* ev = nullptr; // ev[0]: start, ev[1 + i]: stream i done
-    hipError_t e = pipeline_events(&ev);
-    if (e != hipSuccess) return hip_fail(e, "qar_reduce_quantized_pipelined: events");
-    e = hipEventRecord(ev[0], main_st);
-    for (uint32_t i = 0; e == hipSuccess && i < used; ++i)
-        e = hipStreamWaitEvent((hipStream_t)streams[i], ev[0], 0);
-    for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
-        const size_t b0 = c * per;
-        if (b0 >= nb) break;
-        const size_t bn = (nb - b0 < per) ? nb - b0 : per;
-        const size_t e0 = b0 * block;
-        qar::RankPtrs rp;
-        fill_ranks(rp, codes, scales, nranks, e0, b0);
-        void* out_c = out ? (void*)((char*)out + e0 * out_bytes) : nullptr;
-        e = qar::launch_reduce(rp, (int)nranks, bn * block, (int)block, codes_out + e0, scales_out + b0,
-                               out_c, kind, (hipStream_t)streams[c % used]);
-    }
-    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) {
-        e = hipEventRecord(ev[1 + i], (hipStream_t)streams[i]);
-        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, ev[1 + i], 0);
-    }
+        if (!streams[i] && stream) return QAR_ERR_INVALID_ARG;
+    const uint32_t used = streams_used(nchunks, n, block, nstreams);
+    ForkJoin fj((hipStream_t)stream, streams, used);
+    hipError_t e = fj.fork();
+    if (e == hipSuccess)
+        e = chunks_run(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype, nchunks, streams, used);
+    if (e == hipSuccess) e = fj.join();
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_pipelined");
 }
 
@@ -427,58 +516,47 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_unquantized");
 }
 
-qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
-                                   uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
-                                   float* const* scales_work, void* out, uint32_t nchunks,
-                                   void* const* streams, uint32_t nstreams, void* stream) {
-    if (n == 0) return QAR_OK;
+} // extern "C"
+
+namespace {
+
+// Checks shared by both simulated-AllReduce calls: sizes, inputs, output.
+qar_status check_allreduce(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n, uint32_t block,
+                           qar_schedule schedule, void* out, uint32_t nchunks, Range* ins, Range* oo) {
     qar_status st = check_common(n, block);
     if (st != QAR_OK) return st;
     if (schedule != QAR_SCHEDULE_ONE_SHOT && schedule != QAR_SCHEDULE_RING) return QAR_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return QAR_ERR_UNSUPPORTED;
-    if (!x || !codes_work || !scales_work || !out || !streams) return QAR_ERR_INVALID_ARG;
-    if (nranks == 0 || nranks > QAR_MAX_RANKS || nchunks == 0 || nstreams == 0 || nstreams > QAR_MAX_STREAMS)
-        return QAR_ERR_INVALID_ARG;
-    for (uint32_t i = 0; i < nstreams; ++i)
-        if (!streams[i]) return QAR_ERR_INVALID_ARG;
-    const uint32_t nwork = schedule == QAR_SCHEDULE_ONE_SHOT ? nranks : 1;
-    const size_t nb = n / block, eb = dtype_bytes(dtype);
-    // every buffer the call touches; inputs may overlap each other, the
-    // workspaces and the output may overlap nothing
-    Range ins[QAR_MAX_RANKS], outs[2 * QAR_MAX_RANKS + 1];
-    int nouts = 0;
+    if (!x || !out) return QAR_ERR_INVALID_ARG;
+    if (nranks == 0 || nranks > QAR_MAX_RANKS || nchunks == 0) return QAR_ERR_INVALID_ARG;
+    const size_t eb = dtype_bytes(dtype);
     for (uint32_t r = 0; r < nranks; ++r) {
         if (!x[r]) return QAR_ERR_INVALID_ARG;
         if (!aligned(x[r], 16)) return QAR_ERR_MISALIGNED;
         ins[r] = range(x[r], n * eb);
     }
-    for (uint32_t r = 0; r < nwork; ++r) {
-        if (!codes_work[r] || !scales_work[r]) return QAR_ERR_INVALID_ARG;
-        if (!aligned(codes_work[r], 16) || !aligned(scales_work[r], 4)) return QAR_ERR_MISALIGNED;
-        outs[nouts++] = range(codes_work[r], n);
-        outs[nouts++] = range(scales_work[r], nb * 4);
-    }
     if (!aligned(out, 16)) return QAR_ERR_MISALIGNED;
-    outs[nouts++] = range(out, n * eb);
-    for (int i = 0; i < nouts; ++i) {
-        for (int j = i + 1; j < nouts; ++j)
-            if (overlap(outs[i], outs[j])) return QAR_ERR_INVALID_ARG;
-        for (uint32_t r = 0; r < nranks; ++r)
-            if (overlap(outs[i], ins[r])) return QAR_ERR_INVALID_ARG;
-    }
+    *oo = range(out, n * eb);
+    for (uint32_t r = 0; r < nranks; ++r)
+        if (overlap(*oo, ins[r])) return QAR_ERR_INVALID_ARG;
+    return QAR_OK;
+}
 
+// The simulated AllReduce after its checks: chunk c on streams[c % used],
+// staging in codes_work / scales_work (nranks of each for one-shot, [0] for
+// the ring).
+hipError_t allreduce_run(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n, uint32_t block,
+                         qar_schedule schedule, int8_t* const* codes_work, float* const* scales_work, void* out,
+                         uint32_t nchunks, void* const* streams, uint32_t nstreams, hipStream_t main_st) {
+    const size_t nb = n / block, eb = dtype_bytes(dtype);
     const size_t chunks = nchunks < nb ? nchunks : nb;
     const size_t per = (nb + chunks - 1) / chunks;
     const uint32_t used = (uint32_t)(chunks < nstreams ? chunks : nstreams);
     const int kind = dtype == QAR_BF16 ? qar::kInBF16 : qar::kInF32;
     const int okind = dtype == QAR_BF16 ? qar::kOutBF16 : qar::kOutF32;
-    const hipStream_t main_st = (hipStream_t)stream;
 
-    hipEvent_t* ev = nullptr;
-    hipError_t e = pipeline_events(&ev);
-    if (e != hipSuccess) return hip_fail(e, "qar_allreduce_simulated: events");
-    e = hipEventRecord(ev[0], main_st);
-    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) e = hipStreamWaitEvent((hipStream_t)streams[i], ev[0], 0);
+    ForkJoin fj(main_st, streams, used);
+    hipError_t e = fj.fork();
     for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
         const size_t b0 = c * per;
         if (b0 >= nb) break;
@@ -515,10 +593,47 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
             if (e == hipSuccess) e = qar::launch_dequantize(q, sc, cn, (int)block, oc, okind, cs);
         }
     }
-    for (uint32_t i = 0; e == hipSuccess && i < used; ++i) {
-        e = hipEventRecord(ev[1 + i], (hipStream_t)streams[i]);
-        if (e == hipSuccess) e = hipStreamWaitEvent(main_st, ev[1 + i], 0);
+    if (e == hipSuccess) e = fj.join();
+    return e;
+}
+
+} // namespace
+
+extern "C" {
+
+qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
+                                   uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
+                                   float* const* scales_work, void* out, uint32_t nchunks,
+                                   void* const* streams, uint32_t nstreams, void* stream) {
+    if (n == 0) return QAR_OK;
+    Range ins[QAR_MAX_RANKS], oo;
+    qar_status st = check_allreduce(x, dtype, nranks, n, block, schedule, out, nchunks, ins, &oo);
+    if (st != QAR_OK) return st;
+    if (!codes_work || !scales_work || !streams) return QAR_ERR_INVALID_ARG;
+    if (nstreams == 0 || nstreams > QAR_MAX_STREAMS) return QAR_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < nstreams; ++i)
+        if (!streams[i] && stream) return QAR_ERR_INVALID_ARG;
+    const uint32_t nwork = schedule == QAR_SCHEDULE_ONE_SHOT ? nranks : 1;
+    const size_t nb = n / block;
+    // the workspaces and the output may overlap nothing; inputs may overlap
+    // each other
+    Range outs[2 * QAR_MAX_RANKS + 1];
+    int nouts = 0;
+    for (uint32_t r = 0; r < nwork; ++r) {
+        if (!codes_work[r] || !scales_work[r]) return QAR_ERR_INVALID_ARG;
+        if (!aligned(codes_work[r], 16) || !aligned(scales_work[r], 4)) return QAR_ERR_MISALIGNED;
+        outs[nouts++] = range(codes_work[r], n);
+        outs[nouts++] = range(scales_work[r], nb * 4);
     }
+    outs[nouts++] = oo;
+    for (int i = 0; i < nouts; ++i) {
+        for (int j = i + 1; j < nouts; ++j)
+            if (overlap(outs[i], outs[j])) return QAR_ERR_INVALID_ARG;
+        for (uint32_t r = 0; r < nranks; ++r)
+            if (overlap(outs[i], ins[r])) return QAR_ERR_INVALID_ARG;
+    }
+    const hipError_t e = allreduce_run(x, dtype, nranks, n, block, schedule, codes_work, scales_work, out, nchunks,
+                                       streams, nstreams, (hipStream_t)stream);
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_allreduce_simulated");
 }
 

@@ -118,13 +118,25 @@ constexpr float kRoundMagic = 12582912.0f;
 // The quotient x / s, correctly rounded, is computed from the block's
 // reciprocal r = 1/s (one IEEE division per lane) and one FMA correction:
 //   y = x*r;  e = fma(-y, s, x);  y = fma(e, r, y).
-// This equals the IEEE quotient for every pair of binary32 significands
-// (checked exhaustively, all 2^23 x 2^23 pairs), hence for every exponent
-// pair whose intermediates stay normal.  For s >= 2^-100 (s never exceeds
-// FLT_MAX/127 < 2^121) r, y and every remainder that matters are normal or
-// exact, and a quotient below 1/4 in magnitude, whose code is 0 either way,
-// stays below 1/2.  Smaller scales take the IEEE division.
+// This equals the IEEE quotient for every pair of binary32 significands:
+// tests/test_gpu_quotient_exhaustive.py runs this function on all
+// 2^23 x 2^23 pairs and checks each result exactly in binary64 integer
+// arithmetic.  Scaling x and s by powers of two scales every intermediate
+// alike as long as none of them leaves the normal range, so the identity
+// holds for every exponent pair whose intermediates stay normal.  For
+// s >= 2^-100 (s never exceeds FLT_MAX/127 < 2^121) r, y and every
+// remainder that matters are normal or exact, and a quotient below 1/4 in
+// magnitude, whose code is 0 either way, stays below 1/2
+// (tests/test_quotient_exponents.py checks both on sampled pairs against
+// exact rationals, down to the threshold).  Smaller scales take the IEEE
+// division.
 constexpr float kFastQuotientMinScale = 0x1p-100f;
+
+__device__ __forceinline__ float fast_quotient(float x, float s, float r) {
+    const float y = x * r;
+    const float e = __builtin_fmaf(-y, s, x);
+    return __builtin_fmaf(e, r, y);
+}
 
 // On the fast path the clamp to [-Q, Q] can never change a code, so it is
 // left out there.  s = fl(m/Q) is normal, hence s >= (m/Q)(1 - 2^-24), and
@@ -152,12 +164,7 @@ __device__ __forceinline__ uint4 quantize16(const float (&v)[kLaneElems], float 
     if (s >= kFastQuotientMinScale) {
         const float r = 1.0f / s;
 #pragma unroll
-        for (int i = 0; i < kLaneElems; ++i) {
-            float y = v[i] * r;
-            const float e = __builtin_fmaf(-y, s, v[i]);
-            y = __builtin_fmaf(e, r, y);
-            w[i] = code_bits_of(y);
-        }
+        for (int i = 0; i < kLaneElems; ++i) w[i] = code_bits_of(fast_quotient(v[i], s, r));
     } else if (s != 0.0f) {
 #pragma unroll
         for (int i = 0; i < kLaneElems; ++i) w[i] = clamped_code_bits_of(v[i] / s);
@@ -282,12 +289,10 @@ struct E4M3Codes {
             const float r = 1.0f / s;
 #pragma unroll
             for (int i = 0; i < kLaneElems; ++i) {
-                float y = v[i] * r;
-                const float e = __builtin_fmaf(-y, s, v[i]);
                 // x = -0 gives e = +0 and +0 + -0 = +0: put the sign back.
                 // No clamp: as for int8 (code_bits_of), a normal s bounds the
                 // rounded quotient by Q + 2^-15 here.
-                t[i] = __builtin_copysignf(__builtin_fmaf(e, r, y), v[i]);
+                t[i] = __builtin_copysignf(fast_quotient(v[i], s, r), v[i]);
             }
         } else if (s != 0.0f) {
 #pragma unroll
@@ -350,12 +355,8 @@ struct Int4Codes {
         if (s >= kFastQuotientMinScale) {
             const float r = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) {
-                float y = v[i] * r;
-                const float e = __builtin_fmaf(-y, s, v[i]);
-                y = __builtin_fmaf(e, r, y);
-                w[i] = __builtin_bit_cast(uint32_t, y + kRoundMagic); // no clamp needed (see code_bits_of)
-            }
+            for (int i = 0; i < kLaneElems; ++i) // no clamp needed (see code_bits_of)
+                w[i] = __builtin_bit_cast(uint32_t, fast_quotient(v[i], s, r) + kRoundMagic);
         } else if (s != 0.0f) {
 #pragma unroll
             for (int i = 0; i < kLaneElems; ++i)

@@ -16,7 +16,10 @@
 // registers.  A workgroup walks tiles
 // of 4096 elements with a grid-stride loop (the grid is capped, the loop
 // covers any n).
+#include <mutex>
+#include <tuple>
 #include <type_traits>
+#include <utility>
 
 #include "qar_device.h"
 #include "qar_launch.h"
@@ -520,12 +523,7 @@ __device__ __forceinline__ void quantize4(const float (&v)[kRowSlots], float s, 
     if (s >= kFastQuotientMinScale) {
         const float r = 1.0f / s;
 #pragma unroll
-        for (int t = 0; t < kRowSlots; ++t) {
-            float y = v[t] * r;
-            const float e = __builtin_fmaf(-y, s, v[t]);
-            y = __builtin_fmaf(e, r, y);
-            q[t] = (int8_t)(code_bits_of(y) & 0xFFu);
-        }
+        for (int t = 0; t < kRowSlots; ++t) q[t] = (int8_t)(code_bits_of(fast_quotient(v[t], s, r)) & 0xFFu);
     } else if (s != 0.0f) {
 #pragma unroll
         for (int t = 0; t < kRowSlots; ++t) q[t] = (int8_t)(clamped_code_bits_of(v[t] / s) & 0xFFu);
@@ -660,15 +658,34 @@ namespace {
 
 constexpr uint32_t kMaxGrid = 1u << 22;
 
+// Launches k<<<blocks, kThreads, 0, st>>>(a...) and returns that launch's
+// own status.  hipLaunchKernel reports the launch it was asked for; reading
+// hipGetLastError() after a triple-chevron launch would instead return any
+// error an unrelated runtime call had left on the thread.
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), uint32_t blocks, hipStream_t st, A&&... a) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<std::decay_t<P>...> vals(static_cast<std::decay_t<P>>(std::forward<A>(a))...);
+    void* args[sizeof...(P)];
+    std::apply([&](auto&... v) {
+        size_t i = 0;
+        ((args[i++] = static_cast<void*>(&v)), ...);
+    }, vals);
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(blocks), dim3(kThreads), args, 0, st);
+}
+
 struct Grid {
     uint32_t ntiles, blocks;
 };
 
-Grid grid_for(size_t n) {
+// One workgroup per tile, at most `cap` workgroups (0: kMaxGrid); the
+// kernels' grid-stride loops cover the rest.
+Grid grid_for(size_t n, uint32_t cap = 0) {
     const size_t tiles = (n + kTileElems - 1) / kTileElems;
+    const size_t limit = cap ? (cap < kMaxGrid ? cap : kMaxGrid) : kMaxGrid;
     Grid g;
     g.ntiles = (uint32_t)tiles;
-    g.blocks = (uint32_t)(tiles < kMaxGrid ? tiles : kMaxGrid);
+    g.blocks = (uint32_t)(tiles < limit ? tiles : limit);
     return g;
 }
 
@@ -689,56 +706,19 @@ hipError_t dispatch_block(int block, F&& f) {
     }
 }
 
-template <int B, typename Lanes, typename C = Int8Codes>
-hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* codes, float* scales,
-                      hipStream_t st) {
-    if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_quantize<B, uint16_t, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(x), lanes, codes, scales, g.ntiles);
-    else
-        hipLaunchKernelGGL((k_quantize<B, float, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st,
-                           static_cast<const float*>(x), lanes, codes, scales, g.ntiles);
-    return hipGetLastError();
+// calls f(std::integral_constant<int, OUT>) for an output kind
+template <typename F>
+hipError_t dispatch_out(int out_kind, F&& f) {
+    if (out_kind == kOutBF16) return f(std::integral_constant<int, kOutBF16>{});
+    if (out_kind == kOutF32) return f(std::integral_constant<int, kOutF32>{});
+    return f(std::integral_constant<int, kOutNone>{});
 }
 
-template <int B, typename Lanes, typename C = Int8Codes>
-hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t* codes_out, float* scales_out,
-                    void* out, int out_kind, hipStream_t st) {
-    if (out_kind == kOutBF16)
-        hipLaunchKernelGGL((k_reduce<B, kOutBF16, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
-                           lanes, codes_out, scales_out, out, g.ntiles);
-    else if (out_kind == kOutF32)
-        hipLaunchKernelGGL((k_reduce<B, kOutF32, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
-                           lanes, codes_out, scales_out, out, g.ntiles);
-    else
-        hipLaunchKernelGGL((k_reduce<B, kOutNone, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, rp, nranks,
-                           lanes, codes_out, scales_out, out, g.ntiles);
-    return hipGetLastError();
-}
-
-template <int B, typename Lanes, typename C = Int8Codes>
-hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind, Lanes lanes,
-                  Grid g, int8_t* codes_out, float* scales_out, hipStream_t st) {
-    if (in_kind == kInBF16)
-        hipLaunchKernelGGL((k_ring_step<B, uint16_t, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
-                           scales_in, static_cast<const uint16_t*>(local), lanes, codes_out, scales_out, g.ntiles);
-    else
-        hipLaunchKernelGGL((k_ring_step<B, float, Lanes, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes_in,
-                           scales_in, static_cast<const float*>(local), lanes, codes_out, scales_out, g.ntiles);
-    return hipGetLastError();
-}
-
-template <int B, typename C = Int8Codes>
-hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void* out, int out_kind,
-                        hipStream_t st) {
-    const Grid g = grid_for(n);
-    if (out_kind == kOutBF16)
-        hipLaunchKernelGGL((k_dequantize<B, uint16_t, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes,
-                           scales, n, static_cast<uint16_t*>(out), g.ntiles);
-    else
-        hipLaunchKernelGGL((k_dequantize<B, float, C>), dim3(g.blocks), dim3(kThreads), 0, st, codes, scales,
-                           n, static_cast<float*>(out), g.ntiles);
-    return hipGetLastError();
+// calls f(TypeTag<element type>) for an input kind
+template <typename F>
+hipError_t dispatch_in(int in_kind, F&& f) {
+    if (in_kind == kInBF16) return f(TypeTag<uint16_t>{});
+    return f(TypeTag<float>{});
 }
 
 // calls f(TypeTag<codes format>) for a code kind
@@ -747,6 +727,46 @@ hipError_t dispatch_code(int code, F&& f) {
     if (code == kCodeE4M3) return f(TypeTag<E4M3Codes>{});
     if (code == kCodeInt4) return f(TypeTag<Int4Codes>{});
     return f(TypeTag<Int8Codes>{});
+}
+
+template <int B, typename Lanes, typename C = Int8Codes>
+hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* codes, float* scales,
+                      hipStream_t st) {
+    return dispatch_in(in_kind, [&](auto it) {
+        using In = typename decltype(it)::type;
+        return launch(k_quantize<B, In, Lanes, C>, g.blocks, st, static_cast<const In*>(x), lanes, codes, scales,
+                      g.ntiles);
+    });
+}
+
+template <int B, typename Lanes, typename C = Int8Codes>
+hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t* codes_out, float* scales_out,
+                    void* out, int out_kind, hipStream_t st) {
+    return dispatch_out(out_kind, [&](auto oc) {
+        constexpr int OUT = decltype(oc)::value;
+        return launch(k_reduce<B, OUT, Lanes, C>, g.blocks, st, rp, nranks, lanes, codes_out, scales_out, out,
+                      g.ntiles);
+    });
+}
+
+template <int B, typename Lanes, typename C = Int8Codes>
+hipError_t ring_b(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind, Lanes lanes,
+                  Grid g, int8_t* codes_out, float* scales_out, hipStream_t st) {
+    return dispatch_in(in_kind, [&](auto it) {
+        using In = typename decltype(it)::type;
+        return launch(k_ring_step<B, In, Lanes, C>, g.blocks, st, codes_in, scales_in, static_cast<const In*>(local),
+                      lanes, codes_out, scales_out, g.ntiles);
+    });
+}
+
+template <int B, typename C = Int8Codes>
+hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void* out, int out_kind,
+                        hipStream_t st) {
+    const Grid g = grid_for(n);
+    if (out_kind == kOutBF16)
+        return launch(k_dequantize<B, uint16_t, C>, g.blocks, st, codes, scales, n, static_cast<uint16_t*>(out),
+                      g.ntiles);
+    return launch(k_dequantize<B, float, C>, g.blocks, st, codes, scales, n, static_cast<float*>(out), g.ntiles);
 }
 
 template <int B>
@@ -774,17 +794,38 @@ hipError_t rows_vector(const RowsCall& c, hipStream_t st) {
     case kRowsRingStep:
         return ring_b<B>(c.codes_in, c.scales_in, c.x, c.kind, l, g, c.codes_out, c.scales_out, st);
     default:
-        if (c.kind == kInBF16)
-            hipLaunchKernelGGL((k_dequantize_lanes<B, uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st,
-                               c.codes_in, c.scales_in, l, static_cast<uint16_t*>(c.out), g.ntiles);
-        else
-            hipLaunchKernelGGL((k_dequantize_lanes<B, float>), dim3(g.blocks), dim3(kThreads), 0, st, c.codes_in,
-                               c.scales_in, l, static_cast<float*>(c.out), g.ntiles);
-        return hipGetLastError();
+        return dispatch_in(c.kind, [&](auto ot) {
+            using Out = typename decltype(ot)::type;
+            return launch(k_dequantize_lanes<B, Out>, g.blocks, st, c.codes_in, c.scales_in, l,
+                          static_cast<Out*>(c.out), g.ntiles);
+        });
     }
 }
 
 uint32_t row_grid(size_t nblocks) { return (uint32_t)((nblocks + kThreads / 64 - 1) / (kThreads / 64)); }
+
+// Workgroups of a k_reduce instantiation that one device holds at once:
+// compute units times the workgroups per compute unit its registers and LDS
+// allow.  Queried once per device and kernel, then cached.
+constexpr int kCapacityDevices = 64;
+
+template <int B, int OUT, typename C>
+uint32_t reduce_capacity() {
+    static std::once_flag once[kCapacityDevices];
+    static uint32_t cap[kCapacityDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kCapacityDevices) return 0;
+    std::call_once(once[dev], [dev] {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(k_reduce<B, OUT, FlatLanes<B>, C>), kThreads, 0) !=
+                hipSuccess)
+            cus = per_cu = 0;
+        cap[dev] = (uint32_t)(cus > 0 && per_cu > 0 ? cus * per_cu : 0);
+    });
+    return cap[dev];
+}
 
 } // namespace
 
@@ -802,54 +843,33 @@ hipError_t launch_rows(const RowsCall& c, hipStream_t st) {
     map.block = (uint32_t)c.block;
     map.per_row = (uint32_t)((c.row_len + c.block - 1) / c.block);
     const size_t nblocks = c.rows * map.per_row;
-    const dim3 grid(row_grid(nblocks)), threads(kThreads);
-    switch (c.op) {
-    case kRowsQuantize:
-        if (c.kind == kInBF16)
-            hipLaunchKernelGGL((k_quantize_rows<uint16_t>), grid, threads, 0, st, static_cast<const uint16_t*>(c.x),
-                               map, nblocks, c.codes_out, c.scales_out);
-        else
-            hipLaunchKernelGGL((k_quantize_rows<float>), grid, threads, 0, st, static_cast<const float*>(c.x), map,
-                               nblocks, c.codes_out, c.scales_out);
-        break;
-    case kRowsDequantize:
-        if (c.kind == kInBF16)
-            hipLaunchKernelGGL((k_dequantize_rows<uint16_t>), grid, threads, 0, st, c.codes_in, c.scales_in, map,
-                               nblocks, static_cast<uint16_t*>(c.out));
-        else
-            hipLaunchKernelGGL((k_dequantize_rows<float>), grid, threads, 0, st, c.codes_in, c.scales_in, map,
-                               nblocks, static_cast<float*>(c.out));
-        break;
-    case kRowsReduce:
-        if (c.kind == kInBF16)
-            hipLaunchKernelGGL((k_reduce_rows<uint16_t>), grid, threads, 0, st, c.rp, c.nranks, map, nblocks,
-                               c.codes_out, c.scales_out, static_cast<uint16_t*>(c.out));
-        else
-            hipLaunchKernelGGL((k_reduce_rows<float>), grid, threads, 0, st, c.rp, c.nranks, map, nblocks,
-                               c.codes_out, c.scales_out, static_cast<float*>(c.out));
-        break;
-    default:
-        if (c.kind == kInBF16)
-            hipLaunchKernelGGL((k_ring_step_rows<uint16_t>), grid, threads, 0, st, c.codes_in, c.scales_in,
-                               static_cast<const uint16_t*>(c.x), map, nblocks, c.codes_out, c.scales_out);
-        else
-            hipLaunchKernelGGL((k_ring_step_rows<float>), grid, threads, 0, st, c.codes_in, c.scales_in,
-                               static_cast<const float*>(c.x), map, nblocks, c.codes_out, c.scales_out);
-        break;
-    }
-    return hipGetLastError();
+    const uint32_t grid = row_grid(nblocks);
+    return dispatch_in(c.kind, [&](auto it) {
+        using T = typename decltype(it)::type;
+        switch (c.op) {
+        case kRowsQuantize:
+            return launch(k_quantize_rows<T>, grid, st, static_cast<const T*>(c.x), map, nblocks, c.codes_out,
+                          c.scales_out);
+        case kRowsDequantize:
+            return launch(k_dequantize_rows<T>, grid, st, c.codes_in, c.scales_in, map, nblocks,
+                          static_cast<T*>(c.out));
+        case kRowsReduce:
+            return launch(k_reduce_rows<T>, grid, st, c.rp, c.nranks, map, nblocks, c.codes_out, c.scales_out,
+                          static_cast<T*>(c.out));
+        default:
+            return launch(k_ring_step_rows<T>, grid, st, c.codes_in, c.scales_in, static_cast<const T*>(c.x), map,
+                          nblocks, c.codes_out, c.scales_out);
+        }
+    });
 }
 
 hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, int kind, void* out,
                                      hipStream_t st) {
     const Grid g = grid_for(n);
-    if (kind == kInBF16)
-        hipLaunchKernelGGL((k_reduce_unquantized<uint16_t>), dim3(g.blocks), dim3(kThreads), 0, st, xp, nranks, n,
-                           static_cast<uint16_t*>(out), g.ntiles);
-    else
-        hipLaunchKernelGGL((k_reduce_unquantized<float>), dim3(g.blocks), dim3(kThreads), 0, st, xp, nranks, n,
-                           static_cast<float*>(out), g.ntiles);
-    return hipGetLastError();
+    return dispatch_in(kind, [&](auto it) {
+        using T = typename decltype(it)::type;
+        return launch(k_reduce_unquantized<T>, g.blocks, st, xp, nranks, n, static_cast<T*>(out), g.ntiles);
+    });
 }
 
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
@@ -865,14 +885,22 @@ hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8
 }
 
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
-    const Grid g = grid_for(n);
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code, int share) {
     return dispatch_code(code, [&](auto ct) {
         using C = typename decltype(ct)::type;
         return dispatch_block(block, [&](auto bc) {
             constexpr int B = decltype(bc)::value;
-            return reduce_b<B, FlatLanes<B>, C>(rp, nranks, FlatLanes<B>{n}, g, codes_out, scales_out, out,
-                                                out_kind, st);
+            return dispatch_out(out_kind, [&](auto oc) {
+                constexpr int OUT = decltype(oc)::value;
+                uint32_t cap = 0;
+                if (share > 0) {
+                    const uint32_t all = reduce_capacity<B, OUT, C>();
+                    cap = all ? (all + share - 1) / share : 0;
+                }
+                const Grid g = grid_for(n, cap);
+                return launch(k_reduce<B, OUT, FlatLanes<B>, C>, g.blocks, st, rp, nranks, FlatLanes<B>{n},
+                              codes_out, scales_out, out, g.ntiles);
+            });
         });
     });
 }
@@ -881,38 +909,26 @@ hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
                                   float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
     const Grid g = grid_for(n);
+    // dense loads unless the last group of 8 ranks has 1-4 of them
+    const bool dense = nranks % 8 == 0 || nranks % 8 >= 5;
     return dispatch_code(code, [&](auto ct) {
         using C = typename decltype(ct)::type;
         return dispatch_block(block, [&](auto bc) {
             constexpr int B = decltype(bc)::value;
             const FlatLanes<B> lanes{n};
-            // dense loads unless the last group of 8 ranks has 1-4 of them
-            const bool dense = nranks % 8 == 0 || nranks % 8 >= 5;
-            auto go = [&](auto oc, auto in_tag) {
+            return dispatch_out(out_kind, [&](auto oc) {
                 constexpr int OUT = decltype(oc)::value;
-                using In = typename decltype(in_tag)::type;
-                if (dense)
-                    hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C, true>), dim3(g.blocks), dim3(kThreads), 0,
-                                       st, static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks,
-                                       lanes, codes_out, scales_out, out, g.ntiles);
-                else
-                    hipLaunchKernelGGL((k_quantize_reduce<B, OUT, In, C, false>), dim3(g.blocks), dim3(kThreads), 0,
-                                       st, static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks,
-                                       lanes, codes_out, scales_out, out, g.ntiles);
-            };
-            auto with_in = [&](auto oc) {
-                if (in_kind == kInBF16)
-                    go(oc, TypeTag<uint16_t>{});
-                else
-                    go(oc, TypeTag<float>{});
-            };
-            if (out_kind == kOutBF16)
-                with_in(std::integral_constant<int, kOutBF16>{});
-            else if (out_kind == kOutF32)
-                with_in(std::integral_constant<int, kOutF32>{});
-            else
-                with_in(std::integral_constant<int, kOutNone>{});
-            return hipGetLastError();
+                return dispatch_in(in_kind, [&](auto it) {
+                    using In = typename decltype(it)::type;
+                    if (dense)
+                        return launch(k_quantize_reduce<B, OUT, In, C, true>, g.blocks, st,
+                                      static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
+                                      codes_out, scales_out, out, g.ntiles);
+                    return launch(k_quantize_reduce<B, OUT, In, C, false>, g.blocks, st,
+                                  static_cast<const In*>(x_own), own, own_codes, own_scales, rp, nranks, lanes,
+                                  codes_out, scales_out, out, g.ntiles);
+                });
+            });
         });
     });
 }

@@ -52,8 +52,10 @@
  *   - Any block-aligned sub-range of a valid call (pointers advanced by
  *     k*block elements and k scales) is itself a valid call with the same
  *     results in that range.
- *   - Thread-safe; the only global state is per thread: the text behind
- *     qar_last_error() and the pipelined call's cached HIP events.
+ *   - Thread-safe.  Global state: the per-thread text behind
+ *     qar_last_error(), and a per-device pool of HIP events that the calls
+ *     forking work onto side streams borrow while they enqueue (created on
+ *     demand, one set per call in flight at once, never device memory).
  */
 #ifndef QAR_H
 #define QAR_H
@@ -138,18 +140,45 @@ qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own,
                                void* stream);
 
 /*
- * The same reduce, cut into `nchunks` block-aligned chunks that are
- * enqueued round-robin on `streams[0 .. nstreams-1]`, so that one chunk's
- * loads overlap another chunk's arithmetic (the pages' pipelining of
- * communication and compute, "key innovations" item 2 and "key design"
- * item 3, taken on one GPU).  Results are bit-identical to
- * qar_reduce_quantized for every nchunks and nstreams.  Work on the side
- * streams starts after everything already enqueued on `stream`, and
- * `stream` waits for all chunks, so the caller sees one ordered operation on
- * `stream`.  The call's HIP events are created on its first use per thread
- * and device and reused afterwards (never device memory).
+ * The same reduce as a pipeline of chunks over streams (the pages' deep
+ * pipelining of communication and compute, "key innovations" item 2 and
+ * "key design" item 3, taken on one GPU).  The block range is cut into
+ * `nchunks` block-aligned chunks of equal size (the last one shorter), and
+ * chunk c is enqueued on streams[c % nstreams] behind whatever that stream
+ * already holds.  Nothing else is enqueued: no event, no wait.  The caller
+ * orders the chunks after the producers of the inputs and before the
+ * consumers of the outputs on every stream used (events, or by producing
+ * and consuming on those streams).  Consecutive calls on the same streams
+ * therefore overlap: a stream holds its chunk in flight and the next
+ * call's behind it (double buffering), so one stream's kernel ramps up
+ * while another's drains.  Results are bit-identical to
+ * qar_reduce_quantized for every nchunks and nstreams.
  *   nchunks   >= 1 (clipped to the number of blocks).
- *   streams   HOST array of nstreams hipStream_t (as void*), 1 .. QAR_MAX_STREAMS.
+ *   streams   HOST array of nstreams hipStream_t (as void*), 1 .. QAR_MAX_STREAMS;
+ *             NULL (the default stream) is allowed; the first
+ *             min(nchunks, nstreams) are used.
+ */
+qar_status qar_reduce_quantized_chunked(const int8_t* const* codes, const float* const* scales,
+                                        uint32_t nranks, size_t n, uint32_t block,
+                                        int8_t* codes_out, float* scales_out,
+                                        void* out, qar_dtype out_dtype,
+                                        uint32_t nchunks, void* const* streams, uint32_t nstreams);
+
+/*
+ * qar_reduce_quantized_chunked ordered as one operation on `stream`: the
+ * chunks start after everything already enqueued on `stream`, and `stream`
+ * waits for all of them.  A stream of `streams` that is `stream` itself
+ * needs no event; every other one costs an event record and a wait at each
+ * end of the call (on MI355X with ROCm 7 this fork and join cost tens of
+ * microseconds per call, so a sequence of independent reduces is better
+ * enqueued with qar_reduce_quantized_chunked between one fork and one
+ * join).  The events come from a per-device pool (created on first use,
+ * never device memory).  Results are bit-identical to qar_reduce_quantized.
+ *   nchunks   >= 1 (clipped to the number of blocks).
+ *   streams   HOST array of nstreams hipStream_t (as void*),
+ *             1 .. QAR_MAX_STREAMS; an entry may be NULL (the default
+ *             stream) only when `stream` is NULL too, i.e. when it is the
+ *             calling stream.
  */
 qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const float* const* scales,
                                           uint32_t nranks, size_t n, uint32_t block,
@@ -222,8 +251,9 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
  *                [0] is used for RING (the rest may be NULL).
  *   out          [out] n elements of dtype.
  *   nchunks      >= 1 (clipped to the number of blocks); streams: HOST array
- *                of 1..QAR_MAX_STREAMS handles; `stream` orders the whole call
- *                as in qar_reduce_quantized_pipelined.
+ *                of 1..QAR_MAX_STREAMS handles (NULL only when `stream` is
+ *                NULL); `stream` orders the whole call as in
+ *                qar_reduce_quantized_pipelined.
  * Results are bit-identical for every nchunks and nstreams under ONE_SHOT;
  * under RING they depend on nchunks through each chunk's starting rank.
  */

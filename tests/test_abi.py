@@ -137,6 +137,9 @@ def test_pipelined_validation(L):
     assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 0, None) == qar.QAR_ERR_INVALID_ARG
     assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, None, 1, None) == qar.QAR_ERR_INVALID_ARG
     assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 17, None) == qar.QAR_ERR_INVALID_ARG
+    # the default stream (NULL) may stand in streams[] only as the calling stream itself
+    assert p(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, _arr(None), 1, 0x9999) == \
+        qar.QAR_ERR_INVALID_ARG
 
 
 def test_ring_and_dequantize_validation(L):
@@ -188,6 +191,17 @@ def test_allreduce_simulated_validation(L):
     assert f(*bad) == qar.QAR_ERR_MISALIGNED                        # ring needs only [0]; out misaligned
 
 
+def test_chunked_validation(L):
+    f = L.qar_reduce_quantized_chunked
+    codes, scales, streams = _arr(A, B_), _arr(C, D), _arr(0x1234)
+    assert f(None, None, 2, 0, 256, None, None, None, 0, 4, None, 1) == qar.QAR_OK
+    assert f(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 0, streams, 1) == qar.QAR_ERR_INVALID_ARG
+    assert f(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 0) == qar.QAR_ERR_INVALID_ARG
+    assert f(codes, scales, 2, 256, 256, 0x50000, 0x60000, None, 0, 4, streams, 17) == qar.QAR_ERR_INVALID_ARG
+    assert f(codes, scales, 2, 256, 256, 0x50000, 0x60001, None, 0, 4, streams, 1) == qar.QAR_ERR_MISALIGNED
+    assert f(codes, scales, 2, 256, 256, A + 64, 0x60000, None, 0, 4, streams, 1) == qar.QAR_ERR_INVALID_ARG
+
+
 def test_rows_validation(L):
     q = L.qar_quantize_rows
     assert q(A, qar.QAR_BF16, 0, 100, 256, B_, C, None) == qar.QAR_OK
@@ -196,7 +210,12 @@ def test_rows_validation(L):
     assert q(A, qar.QAR_F32, 3, 100, 256, B_, C + 2, None) == qar.QAR_ERR_MISALIGNED
     assert q(A, qar.QAR_BF16, 3, 100, 256, A + 64, C, None) == qar.QAR_ERR_INVALID_ARG   # codes overlap x
     assert q(A, qar.QAR_BF16, 1 << 20, 1 << 21, 64, B_, C, None) == qar.QAR_ERR_INVALID_ARG   # too many elements
-    assert q(A, qar.QAR_BF16, 1 << 17, 1 << 12, 64, B_, C, None) == qar.QAR_ERR_INVALID_ARG   # too many blocks
+    # too many blocks: 2^26 rows of 100 elements, 2 blocks of 64 per row = 2^27 > QAR_MAX_ROW_BLOCKS, while
+    # 6.7e9 elements stay under QAR_MAX_ELEMENTS; 100 % 64 != 0, so the flat path cannot take it.  The fake
+    # ranges are disjoint (x spans 12.5 GiB from A), so the block cap is the only check that can refuse it.
+    far_codes, far_scales = 1 << 44, 1 << 45
+    assert q(A, qar.QAR_BF16, 1 << 26, 100, 64, far_codes, far_scales, None) == qar.QAR_ERR_INVALID_ARG
+    assert q(A, qar.QAR_BF16, 1 << 25, 100, 64, far_codes, far_scales + 2, None) == qar.QAR_ERR_MISALIGNED  # at the cap
     d = L.qar_dequantize_rows
     assert d(A, C, 3, 100, 256, A + 8, qar.QAR_F32, None) == qar.QAR_ERR_INVALID_ARG        # out overlaps codes
     r = L.qar_reduce_quantized_rows

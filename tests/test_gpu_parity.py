@@ -208,6 +208,67 @@ def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
     assert_same_f32(to_host(out), oracle_lib.dequantize(wc, ws, block, "f32"), "out")
 
 
+@pytest.mark.parametrize("with_caller", [False, True])
+@pytest.mark.parametrize("nchunks,nstreams", [(1, 1), (3, 2), (8, 4), (16, 4), (5, 16)])
+def test_chunked_bit_identical(oracle_lib, nchunks, nstreams, with_caller):
+    """qar_reduce_quantized_chunked: chunk c on streams[c % S] with no event
+    of its own; the caller forks the streams off the current one, runs two
+    calls back to back (the second reusing the first's output buffers, as a
+    pipelined sequence of reduces does) and joins them."""
+    block, nranks = 64, 5
+    n = ragged_n(block, tiles=6)
+    xs = [mixed_f32(710 + r, n, block, SUM_OUTLIER) for r in range(nranks)]
+    codes, scales = _rank_codes(oracle_lib, xs, block)
+    dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
+    cur = torch.cuda.current_stream()
+    streams = ([cur] if with_caller else []) + [torch.cuda.Stream() for _ in range(nstreams - with_caller)]
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    co = torch.empty(n, dtype=torch.int8, device="cuda:0")
+    so = torch.empty(n // block, dtype=torch.float32, device="cuda:0")
+    say(f"chunked nchunks={nchunks} nstreams={nstreams} with_caller={with_caller}")
+    fork = torch.cuda.Event()
+    fork.record(cur)
+    for st in streams:
+        st.wait_event(fork)
+    qar.qar_reduce_quantized_chunked(dc[::-1], ds[::-1], block, nchunks, streams, co, so)   # overwritten next
+    qar.qar_reduce_quantized_chunked(dc, ds, block, nchunks, streams, co, so, out=out)
+    for st in streams:
+        done = torch.cuda.Event()
+        done.record(st)
+        cur.wait_event(done)
+    torch.cuda.synchronize()
+    wc, ws = oracle_lib.reduce(codes, scales, block)
+    assert_same_codes(to_host(co), wc, "codes")
+    assert_same_f32(to_host(so), ws, "scales")
+    assert_same_bits16(to_host(out), oracle_lib.dequantize(wc, ws, block, "bf16"), "out")
+
+
+def test_stale_runtime_error_does_not_fail_a_good_call():
+    """A launch reports its own status: an error an unrelated HIP call left
+    on the thread (an invalid hipSetDevice) must not turn a valid libqar
+    call into QAR_ERR_HIP."""
+    import ctypes
+    # the HIP runtime this process already runs (torch's copy, which libqar
+    # binds to by its soname), not another instance of it
+    maps = open("/proc/self/maps").read().split()
+    hip = ctypes.CDLL(next(p for p in maps if "libamdhip64.so" in p))
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    x = torch.ones(4096, dtype=torch.bfloat16, device="cuda:0")
+    L = qar.lib()
+    codes = torch.empty(4096, dtype=torch.int8, device="cuda:0")
+    scales = torch.empty(16, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    # every tensor exists before the error is planted: torch checks the
+    # thread's last error after its own launches
+    assert hip.hipSetDevice(1 << 20) != 0                # hipErrorInvalidDevice, left on the thread
+    st = L.qar_quantize_blocks(x.data_ptr(), qar.QAR_BF16, 4096, 256, codes.data_ptr(), scales.data_ptr(), stream)
+    assert st == qar.QAR_OK, L.qar_last_error()
+    hip.hipGetLastError()                                 # clear what the test left behind
+    torch.cuda.synchronize()
+    assert bool((codes == 127).all()) and bool((scales == 1.0 / 127).all())
+
+
 # ----------------------------------------------------------------------------
 # ring step
 
