@@ -14,6 +14,7 @@
 #include "qar_launch.h"
 
 static_assert(QAR_MAX_RANKS == qar::kMaxRanks, "rank limit mismatch");
+static_assert(QAR_STATIC_WORKSPACE_BYTES == qar::kStaticWorkspaceBytes, "static workspace size mismatch");
 
 namespace {
 
@@ -205,6 +206,7 @@ const char* qar_status_string(qar_status s) {
     case QAR_ERR_MISALIGNED: return "misaligned pointer";
     case QAR_ERR_UNSUPPORTED: return "unsupported block size or dtype";
     case QAR_ERR_HIP: return "HIP runtime error";
+    case QAR_ERR_CAPACITY: return "the call needs more static workspace than QAR_STATIC_WORKSPACE_BYTES";
     }
     return "unknown status";
 }
@@ -597,6 +599,21 @@ hipError_t allreduce_run(const void* const* x, qar_dtype dtype, uint32_t nranks,
     return e;
 }
 
+// Byte offsets of the staging inside the static workspace: rank r's codes at
+// r * code_stride, its scales at nwork * code_stride + r * scale_stride; both
+// strides are multiples of 256 bytes.
+struct StaticLayout {
+    size_t code_stride, scale_stride, bytes;
+};
+
+StaticLayout static_layout(uint32_t nwork, size_t n, size_t nb) {
+    StaticLayout l;
+    l.code_stride = (n + 255) / 256 * 256;
+    l.scale_stride = (nb * 4 + 255) / 256 * 256;
+    l.bytes = nwork * (l.code_stride + l.scale_stride);
+    return l;
+}
+
 } // namespace
 
 extern "C" {
@@ -635,6 +652,37 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
     const hipError_t e = allreduce_run(x, dtype, nranks, n, block, schedule, codes_work, scales_work, out, nchunks,
                                        streams, nstreams, (hipStream_t)stream);
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_allreduce_simulated");
+}
+
+qar_status qar_allreduce_simulated_static(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
+                                          uint32_t block, qar_schedule schedule, void* out, uint32_t nchunks,
+                                          void* stream) {
+    if (n == 0) return QAR_OK;
+    Range ins[QAR_MAX_RANKS], oo;
+    qar_status st = check_allreduce(x, dtype, nranks, n, block, schedule, out, nchunks, ins, &oo);
+    if (st != QAR_OK) return st;
+    const uint32_t nwork = schedule == QAR_SCHEDULE_ONE_SHOT ? nranks : 1;
+    const size_t nb = n / block;
+    const StaticLayout l = static_layout(nwork, n, nb);
+    if (l.bytes > QAR_STATIC_WORKSPACE_BYTES) {
+        snprintf(g_last_error, sizeof g_last_error,
+                 "qar_allreduce_simulated_static: needs %zu bytes of static workspace, the limit is %zu", l.bytes,
+                 (size_t)QAR_STATIC_WORKSPACE_BYTES);
+        return QAR_ERR_CAPACITY;
+    }
+    uint8_t* base = nullptr;
+    const hipError_t ew = qar::static_workspace(&base);
+    if (ew != hipSuccess) return hip_fail(ew, "qar_allreduce_simulated_static: workspace address");
+    int8_t* codes_work[QAR_MAX_RANKS];
+    float* scales_work[QAR_MAX_RANKS];
+    for (uint32_t r = 0; r < nwork; ++r) {
+        codes_work[r] = reinterpret_cast<int8_t*>(base + r * l.code_stride);
+        scales_work[r] = reinterpret_cast<float*>(base + nwork * l.code_stride + r * l.scale_stride);
+    }
+    void* const streams[1] = {stream};
+    const hipError_t e = allreduce_run(x, dtype, nranks, n, block, schedule, codes_work, scales_work, out, nchunks,
+                                       streams, 1, (hipStream_t)stream);
+    return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_allreduce_simulated_static");
 }
 
 } // extern "C"

@@ -829,6 +829,36 @@ uint32_t reduce_capacity() {
 
 } // namespace
 
+// ---------------------------------------------------------------------------
+// static workspace of the no-allocation entry point
+//
+// One array per device, created when the code object is loaded there and
+// kept until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device (that device current) and only that address is handed to kernels.
+__device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+uint8_t* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+} // namespace
+
+hipError_t static_workspace(uint8_t** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<uint8_t*>(p) : nullptr;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
+
 hipError_t launch_rows(const RowsCall& c, hipStream_t st) {
     if (c.vector) {
         switch (c.block) {

@@ -63,6 +63,12 @@ hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const
 hipError_t launch_ring_step(const int8_t* codes_in, const float* scales_in, const void* local, int in_kind,
                             size_t n, int block, int8_t* codes_out, float* scales_out, hipStream_t st,
                             int code = kCodeInt8);
+// The static workspace (a device array of kStaticWorkspaceBytes per device,
+// 256-byte aligned): its device address on the current device, looked up on
+// the first call per device and cached.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
+hipError_t static_workspace(uint8_t** ptr);
+
 hipError_t launch_dequantize(const int8_t* codes, const float* scales, size_t n, int block, void* out,
                              int out_kind, hipStream_t st, int code = kCodeInt8);
 

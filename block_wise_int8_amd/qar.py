@@ -17,11 +17,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libqar.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qar.h")
 
-QAR_OK, QAR_ERR_INVALID_ARG, QAR_ERR_MISALIGNED, QAR_ERR_UNSUPPORTED, QAR_ERR_HIP = range(5)
+QAR_OK, QAR_ERR_INVALID_ARG, QAR_ERR_MISALIGNED, QAR_ERR_UNSUPPORTED, QAR_ERR_HIP, QAR_ERR_CAPACITY = range(6)
 QAR_BF16, QAR_F32 = 0, 1
 QAR_SCHEDULE_ONE_SHOT, QAR_SCHEDULE_RING = 0, 1
 QAR_MAX_RANKS = 32
 QAR_MAX_STREAMS = 16
+QAR_STATIC_WORKSPACE_BYTES = 64 << 20
 BLOCK_SIZES = (64, 128, 256)
 
 _vp, _sz, _u32, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
@@ -40,6 +41,7 @@ _SIGNATURES = {
     "qar_ring_step_rows": [_vp, _vp, _vp, _int, _sz, _sz, _u32, _vp, _vp, _vp],
     "qar_dequantize_rows": [_vp, _vp, _sz, _sz, _u32, _vp, _int, _vp],
     "qar_allreduce_simulated": [_vp, _int, _u32, _sz, _u32, _int, _vp, _vp, _vp, _u32, _vp, _u32, _vp],
+    "qar_allreduce_simulated_static": [_vp, _int, _u32, _sz, _u32, _int, _vp, _u32, _vp],
     "qar_quantize_blocks_e4m3": [_vp, _int, _sz, _u32, _vp, _vp, _vp],
     "qar_reduce_quantized_e4m3": [_vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
     "qar_quantize_reduce_e4m3": [_vp, _int, _u32, _vp, _vp, _u32, _sz, _u32, _vp, _vp, _vp, _int, _vp],
@@ -60,7 +62,7 @@ class QarError(RuntimeError):
         self.status = status
         L = lib()
         text = L.qar_status_string(status).decode()
-        detail = L.qar_last_error().decode() if status == QAR_ERR_HIP else ""
+        detail = L.qar_last_error().decode() if status in (QAR_ERR_HIP, QAR_ERR_CAPACITY) else ""
         super().__init__(f"{where}: {text}" + (f" ({detail})" if detail else ""))
 
 
@@ -488,6 +490,28 @@ def qar_allreduce_simulated(xs: list[torch.Tensor], block: int, schedule: str = 
                                          ctypes.cast(cp, _vp), ctypes.cast(sp, _vp), _dev(out, "out").data_ptr(),
                                          nchunks, ctypes.cast(sts, _vp), len(streams), _stream(stream)),
            "qar_allreduce_simulated")
+    return out
+
+
+def qar_allreduce_simulated_static(xs: list[torch.Tensor], block: int, schedule: str = "one_shot",
+                                   nchunks: int = 1, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """qar_allreduce_simulated on one stream with its staging in libqar's
+    static device workspace (the library allocates nothing; ``out`` is
+    allocated here with torch when not given)."""
+    if not xs:
+        raise ValueError("need at least one rank")
+    sched = {"one_shot": QAR_SCHEDULE_ONE_SHOT, "ring": QAR_SCHEDULE_RING}[schedule]
+    n, dt, dev = _dev(xs[0], "x[0]").numel(), xs[0].dtype, xs[0].device
+    for r, x in enumerate(xs):
+        _expect(x, f"x[{r}]", n, (dt,), dev)
+    if out is None:
+        out = torch.empty(n, dtype=dt, device=dev)
+    else:
+        _expect(out, "out", n, (dt,), dev)
+    xp = _ptrs(xs)
+    _check(lib().qar_allreduce_simulated_static(ctypes.cast(xp, _vp), _dtype_code(dt), len(xs), n, block, sched,
+                                                out.data_ptr(), nchunks, _stream(stream)),
+           "qar_allreduce_simulated_static")
     return out
 
 

@@ -31,7 +31,9 @@
  *
  * Conventions shared by every call:
  *   - Pointers are device pointers owned by the caller.  libqar never
- *     allocates, frees or synchronizes device memory.
+ *     allocates, frees or synchronizes device memory at run time (its one
+ *     static device array, the workspace of qar_allreduce_simulated_static,
+ *     is part of the loaded code object).
  *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
  *     passed as void*; NULL is the default stream) and the call returns.
  *   - Arguments are checked before anything is enqueued.  A failed check
@@ -53,9 +55,10 @@
  *     k*block elements and k scales) is itself a valid call with the same
  *     results in that range.
  *   - Thread-safe.  Global state: the per-thread text behind
- *     qar_last_error(), and a per-device pool of HIP events that the calls
+ *     qar_last_error(); a per-device pool of HIP events that the calls
  *     forking work onto side streams borrow while they enqueue (created on
- *     demand, one set per call in flight at once, never device memory).
+ *     demand, one set per call in flight at once, never device memory); and
+ *     the static workspace of qar_allreduce_simulated_static.
  */
 #ifndef QAR_H
 #define QAR_H
@@ -72,7 +75,8 @@ typedef enum qar_status {
     QAR_ERR_INVALID_ARG = 1, /* null pointer, n % block != 0, bad rank count, overlap */
     QAR_ERR_MISALIGNED = 2,  /* a pointer breaks the alignment rule above */
     QAR_ERR_UNSUPPORTED = 3, /* block size or dtype outside what is built */
-    QAR_ERR_HIP = 4          /* the HIP runtime refused a launch or call */
+    QAR_ERR_HIP = 4,         /* the HIP runtime refused a launch or call */
+    QAR_ERR_CAPACITY = 5     /* the call needs more static workspace than QAR_STATIC_WORKSPACE_BYTES */
 } qar_status;
 
 typedef enum qar_dtype {
@@ -263,6 +267,34 @@ qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32
                                    uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
                                    float* const* scales_work, void* out, uint32_t nchunks,
                                    void* const* streams, uint32_t nstreams, void* stream);
+
+/*
+ * For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  qar_allreduce_simulated
+ * with the same arguments minus the workspaces and the side streams: every
+ * chunk runs on `stream` in chunk order, and the per-rank code and scale
+ * staging lives in a static device array inside libqar,
+ * QAR_STATIC_WORKSPACE_BYTES per device, held by every device the library
+ * runs on until the process ends.  The call allocates nothing, records no
+ * event and synchronizes nothing; results are bit-identical to
+ * qar_allreduce_simulated with the same schedule and nchunks.
+ *   Capacity: one-shot stages nranks * (n + 4 n/block) bytes, the ring
+ *   n + 4 n/block (each rounded up to 256 bytes per rank and array); a
+ *   call that needs more returns QAR_ERR_CAPACITY and enqueues nothing
+ *   (qar_last_error() gives the sizes).
+ *   Sharing: all calls on one device use the same array.  Calls whose work
+ *   overlaps in time on one device (on different streams, or from several
+ *   threads without ordering between their streams) race on it; order them
+ *   on one stream or with events.  Nothing in the array needs to start at
+ *   zero: every byte a call reads there was written earlier by that call.
+ *   The device address of the array is looked up on the first call per
+ *   device (hipGetSymbolAddress) and cached.
+ */
+#define QAR_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+qar_status qar_allreduce_simulated_static(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
+                                          uint32_t block, qar_schedule schedule, void* out, uint32_t nchunks,
+                                          void* stream);
 
 /*
  * Row-bounded blocks: the same four operations on a [rows, row_len] tensor

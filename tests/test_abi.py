@@ -21,7 +21,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings(L):
-    for s in range(5):
+    for s in range(6):
         assert L.qar_status_string(s)
     assert L.qar_last_error() == b""
 
@@ -189,6 +189,22 @@ def test_allreduce_simulated_validation(L):
     bad = list(ok_args); bad[5] = qar.QAR_SCHEDULE_RING; bad[6] = _arr(C, None); bad[7] = _arr(0x50000, None)
     bad[8] = 0x70001
     assert f(*bad) == qar.QAR_ERR_MISALIGNED                        # ring needs only [0]; out misaligned
+
+
+def test_static_allreduce_validation(L):
+    f = L.qar_allreduce_simulated_static
+    far_out = 1 << 44
+    assert f(None, qar.QAR_BF16, 2, 0, 256, qar.QAR_SCHEDULE_ONE_SHOT, None, 1, None) == qar.QAR_OK   # empty call
+    assert f(_arr(A, B_), qar.QAR_BF16, 2, 256, 100, 0, far_out, 1, None) == qar.QAR_ERR_UNSUPPORTED
+    assert f(_arr(A, B_), qar.QAR_BF16, 2, 256, 256, 7, far_out, 1, None) == qar.QAR_ERR_UNSUPPORTED    # schedule
+    assert f(_arr(A, B_), qar.QAR_BF16, 2, 256, 256, 0, far_out, 0, None) == qar.QAR_ERR_INVALID_ARG    # nchunks
+    assert f(_arr(A, B_), qar.QAR_BF16, 2, 256, 256, 0, A + 64, 1, None) == qar.QAR_ERR_INVALID_ARG     # out on x
+    assert f(_arr(A, B_ + 8), qar.QAR_BF16, 2, 256, 256, 0, far_out, 1, None) == qar.QAR_ERR_MISALIGNED
+    # staging beyond QAR_STATIC_WORKSPACE_BYTES: one-shot over 2 ranks of 2^25 elements needs 2 x 33.6 MB
+    n = 1 << 25
+    assert f(_arr(A, A), qar.QAR_BF16, 2, n, 256, qar.QAR_SCHEDULE_ONE_SHOT, far_out, 1, None) == \
+        qar.QAR_ERR_CAPACITY
+    assert b"static workspace" in L.qar_last_error()
 
 
 def test_chunked_validation(L):
