@@ -108,6 +108,11 @@ def parse():
                         "and block sizes, one JSON line per point")
     p.add_argument("--counter-run", action="store_true",
                    help="only launch every hot-path kernel 4 times over rotated buffers (for rocprofv3 --pmc passes)")
+    p.add_argument("--summarize-trace", metavar="DIR", default=None,
+                   help="no GPU: summarize the rocprofv3 kernel trace of a bench.py --no-extras --no-cpu-baseline run "
+                        "(of --steps steps) under DIR into profiles/")
+    p.add_argument("--bench-json", metavar="PATH", default=None,
+                   help="with --summarize-counters: a bench.py JSON line whose timings fill the achieved columns")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="no GPU: read the rocprofv3 --pmc CSVs of the four counter passes under DIR "
                         "(pmc_copy_fetch, pmc_copy_write, pmc_fetch, pmc_write) and write the traffic summary "
@@ -321,7 +326,7 @@ def counter_run(qar, torch, synth, dev) -> int:
     return 0
 
 
-def summarize_counters(d: str, out_dir: str = PROFILES) -> int:
+def summarize_counters(d: str, out_dir: str = PROFILES, bench_json: str | None = None) -> int:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every catalogue kernel
     from the four passes' CSVs under d (pmc_copy_fetch, pmc_copy_write:
     a 1 GiB device copy; pmc_fetch, pmc_write: --counter-run), scaled by
@@ -381,8 +386,228 @@ def summarize_counters(d: str, out_dir: str = PROFILES) -> int:
         json.dump({"kernel": DOMINANT, "workload": k2["what"], "kernel_source_sha256_16": sha,
                    "calibration": calib, "hbm_bytes_per_launch": k2["hbm_read_bytes"] + k2["hbm_write_bytes"],
                    "traffic_over_algorithmic": k2["traffic_over_algorithmic"]}, f, indent=1)
+    achieved = _achieved_from_bench(bench_json) if bench_json else {}
+    _write_traffic_md(os.path.join(out_dir, "hbm_traffic_all_kernels.md"), rec, achieved, bench_json)
+    if os.path.isdir(os.path.join(d, "pmc_sq")):
+        _write_sq_md(os.path.join(out_dir, "sq_counters_all_kernels.md"), rows_of("pmc_sq"), achieved)
     print(json.dumps(rec, indent=1))
     return 0
+
+
+def summarize_trace(d: str, steps: int, out_dir: str = PROFILES, bench_json: str | None = None) -> int:
+    """The headline step in a rocprofv3 --kernel-trace database under d (a
+    run of bench.py --no-extras --no-cpu-baseline with `steps` timed steps):
+    its last steps * CHUNKS dispatches of the chunked reduce kernel are the
+    timed region.  Writes the span per step (first start to last end over
+    the region, divided by steps), the mean dispatch duration, how the
+    dispatches spread over the hardware queues, and how many run at once."""
+    import glob
+    import sqlite3
+    import statistics
+    dbs = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    name = "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>"
+    con = sqlite3.connect(dbs[0])
+    rows = [r for r in con.execute("select name, start, end, queue_id, grid_x from kernels order by start")
+            if name in r[0]]
+    timed = rows[-steps * CHUNKS:]
+    t0, t1 = timed[0][1], max(r[2] for r in timed)
+    span_us = (t1 - t0) / steps / 1e3
+    durs = [(r[2] - r[1]) / 1e3 for r in timed]
+    queues = {}
+    for r in timed:
+        queues[r[3]] = queues.get(r[3], 0) + 1
+    # dispatches in flight, averaged over the region
+    events = sorted([(r[1], 1) for r in timed] + [(r[2], -1) for r in timed])
+    busy = acc = 0.0
+    level, last = 0, events[0][0]
+    for t, dl in events:
+        acc += level * (t - last)
+        busy += (t - last) if level else 0
+        level += dl
+        last = t
+    w = [k for k in counter_catalogue() if k[0] == "smallblock_reduce_chunk"][0]
+    step_bytes = CHUNKS * (w[4] + w[5])
+    lines = [
+        "# Kernel trace of the headline step: the small-block fused reduce, 8 chunks over 4 streams",
+        "",
+        "One MI355X.  Command (repository root):",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats -d {d} -o run -- python -u bench.py --no-extras --no-cpu-baseline"
+        + (f" > {bench_json}" if bench_json else ""),
+        f"python bench.py --summarize-trace {d}" + (f" --bench-json {bench_json}" if bench_json else ""),
+        "```",
+        "",
+        f"Workload: N=16 ranks x 67,108,864 elements, block 64; each step one `qar_reduce_quantized_chunked` call,",
+        f"{CHUNKS} chunks of `{name}` over {STREAMS} streams (the caller's and 3 side streams).  The timed region is",
+        f"the last {steps} steps ({len(timed)} dispatches).",
+        "",
+        "| figure | value |",
+        "|---|---|",
+        f"| span of the timed region per step | {span_us:.2f} us |",
+        f"| algorithmic bytes per step | {step_bytes:,} |",
+        f"| rate over the span | {step_bytes / (span_us * 1e-6) / 1e12:.3f} TB/s = "
+        f"{100 * step_bytes / (span_us * 1e-6) / 8e12:.1f}% of 8 TB/s |",
+        f"| mean dispatch duration | {statistics.mean(durs):.2f} us (min {min(durs):.2f}, max {max(durs):.2f}) |",
+        f"| dispatches in flight, mean over the region | {acc / (t1 - t0):.2f} |",
+        f"| share of the region with no dispatch in flight | {100 * (1 - busy / (t1 - t0)):.2f}% |",
+        "| dispatches per hardware queue | " + ", ".join(f"queue {q}: {c}" for q, c in sorted(queues.items())) + " |",
+    ]
+    if bench_json:
+        with open(bench_json) as f:
+            rec = json.loads([ln for ln in f.read().splitlines() if ln.strip()][-1])
+        ev = rec["roofline"]["step_us"]
+        lines.append(f"| the same run's HIP events (bench.py `roofline.step_us`) | {ev:.2f} us per step "
+                     f"({100 * (span_us / ev - 1):+.1f}% from the trace span) |")
+    lines += [
+        "",
+        "A chunk's dispatch runs about four times as long as an eighth of the step because four chunks share the",
+        "chip at any time; the rate is the step's bytes over the span, which bench.py measures with HIP events on",
+        "the caller's stream around the same steps (the `roofline` object of its JSON line).",
+    ]
+    with open(os.path.join(out_dir, "k_reduce_smallblock_chunked_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
+# where bench.py's JSON line holds each catalogue kernel's time per launch
+# (median of event-bracketed segments); the chunked step's is per step of
+# CHUNKS launches
+_BENCH_TIMES = {
+    "smallblock_reduce_chunk": (("roofline", "step_us"),),
+    "smallblock_quantize": (("smallblock_quantize", "avg_us"),),
+    "outliers_step": (("outliers_step", "kernels", "k_quantize_reduce (the step)", "avg_us"),),
+    "outliers_quantize": (("outliers_step", "kernels", "k_quantize", "avg_us"),),
+    "outliers_reduce": (("reduce_only", "avg_us"),),
+    "outliers_reduce_bf16": (("outliers_step", "kernels", "k_reduce (bf16 out)", "avg_us"),),
+    "outliers_dequantize": (("dequantize", "avg_us"),),
+    "outliers_comparator": (("unquantized_comparator", "avg_us"),),
+    "outliers_reduce_e4m3": (("code_formats", "timing_outliers", "e4m3", "reduce_no_out", "avg_us"),),
+    "outliers_step_e4m3": (("code_formats", "timing_outliers", "e4m3", "one_kernel_step", "avg_us"),),
+    "outliers_reduce_int4": (("code_formats", "timing_outliers", "int4", "reduce_no_out", "avg_us"),),
+    "outliers_step_int4": (("code_formats", "timing_outliers", "int4", "one_kernel_step", "avg_us"),),
+    "prefill_reduce": (("prefill", "reduce_only", "avg_us"),),
+    "prefill_reduce_bf16": (("prefill", "avg_us"),),
+    "ring_step": (("ring_step", "graph_replay", "avg_us"),),
+    "ring_quantize": (("ring_step", "quantize", "avg_us"),),
+}
+
+
+def _achieved_from_bench(path):
+    """Catalogue key -> (us per launch, algorithmic bytes per launch) from a
+    bench.py JSON line (the chunked step's time divided over its launches'
+    bytes: bytes per step over time per step)."""
+    with open(path) as f:
+        rec = json.loads([ln for ln in f.read().splitlines() if ln.strip()][-1])
+    out = {}
+    for key, (where,) in _BENCH_TIMES.items():
+        v = rec
+        for k in where:
+            v = v.get(k) if isinstance(v, dict) else None
+        if isinstance(v, (int, float)):
+            out[key] = float(v)
+    return out
+
+
+def _write_traffic_md(path, rec, achieved, bench_json):
+    cal = rec["calibration"]
+    lines = [
+        "# HBM traffic of every hot-path kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
+        "",
+        "One MI355X.  Each counter in its own pass over `bench.py --counter-run`, which launches every kernel",
+        "4 times (the small-block chunk 16 times: 2 steps of 8 chunks) over rotated buffer sets, so that no",
+        "launch finds its inputs in L2; the last 4 (16) dispatches of each kernel and grid are averaged.",
+        "Commands (repository root):",
+        "",
+        "```",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o c -- python -u bench.py --copy-probe-mib 1024",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o c -- python -u bench.py --copy-probe-mib 1024",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o b -- python -u bench.py --counter-run",
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o b -- python -u bench.py --counter-run",
+        "python bench.py --summarize-counters gpurun_out" + (f" --bench-json {bench_json}" if bench_json else ""),
+        "```",
+        "",
+        f"Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`, {cal['copy_dispatches']} dispatches) reads and "
+        f"writes 1,048,576 KiB; FETCH_SIZE reads {cal['fetch_kib_raw']:,} KiB per dispatch (factor {cal['fetch_factor']}),",
+        f"WRITE_SIZE {cal['write_kib_raw']:,} KiB (factor {cal['write_factor']}).  Kernel sources hash "
+        f"`{rec['kernel_source_sha256_16']}` (bench.py compares it before using these figures).",
+        "",
+        "Achieved: algorithmic bytes over the kernel's time per launch in the bench.py run named above (median",
+        "of event-bracketed segments of back-to-back launches over rotated sets, behind 50 ms of the same",
+        "launches; the small-block chunk: the step's 8 launches over the step's time).",
+        "",
+        "| kernel | what | read (calibrated) | written | algorithmic read | algorithmic write | traffic / algorithmic"
+        " | us per launch | achieved TB/s | % of 8 TB/s |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for key, k in rec["kernels"].items():
+        alg = k["algorithmic_read_bytes"] + k["algorithmic_write_bytes"]
+        us = achieved.get(key)
+        per = CHUNKS if key == "smallblock_reduce_chunk" else 1
+        if us:
+            tbs = alg * per / (us * 1e-6) / 1e12
+            t = f"{us:.2f}" + (f" per step of {per}" if per > 1 else "")
+            cols = f"{t} | {tbs:.2f} | {100 * tbs / 8:.1f}%"
+        else:
+            cols = "— | — | —"
+        lines.append(f"| `{k['kernel']}` | {k['what']} | {k['hbm_read_bytes']:,} | {k['hbm_write_bytes']:,} | "
+                     f"{k['algorithmic_read_bytes']:,} | {k['algorithmic_write_bytes']:,} | "
+                     f"{k['traffic_over_algorithmic']} | {cols} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _write_sq_md(path, rows, achieved):
+    """SQ counters per catalogue kernel (means over its measured dispatches)."""
+    import statistics
+    lines = [
+        "# SQ counters of every hot-path kernel",
+        "",
+        "One MI355X; one pass with 8 SQ counters and 1 GRBM counter over `bench.py --counter-run`:",
+        "",
+        "```",
+        "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY "
+        "SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_sq -o b -- "
+        "python -u bench.py --counter-run",
+        "```",
+        "",
+        "Means over the last 4 dispatches of each kernel and grid (16 for the small-block chunk).  Counter collection",
+        "serializes dispatches, so the GUI cycles are those of a lone dispatch.  GRBM_GUI_ACTIVE is divided by",
+        "the 8 XCDs for one XCD's busy cycles.  VALU busy = 100 * SQ_ACTIVE_INST_VALU / 256 CUs / GUI cycles;",
+        "waves per CU (average over the dispatch) = 4 * SQ_WAVE_CYCLES / GUI cycles / 256 CUs, of 32 wave slots",
+        "per CU (8 per SIMD); waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.  VALU issue time = SQ_INSTS_VALU /",
+        "(256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles per wave64 instruction), to set against the measured time per",
+        "launch (bench.py, as in `hbm_traffic_all_kernels.md`).",
+        "",
+        "| kernel | waves | VALU instr per wave | loads / stores per wave | GUI cycles (one XCD) | VALU busy |"
+        " waves per CU | waiting | VALU issue us | measured us |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for key, what, name, grid, alg_r, alg_w in counter_catalogue():
+        last = 2 * CHUNKS if key == "smallblock_reduce_chunk" else 4
+        ids = sorted({int(r["Dispatch_Id"]) for r in rows if name in r["Kernel_Name"] and int(r["Grid_Size"]) == grid})
+        ids = set(ids[-last:])
+        c = {}
+        for ctr in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
+                    "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "GRBM_GUI_ACTIVE"):
+            v = [float(r["Counter_Value"]) for r in rows if int(r["Dispatch_Id"]) in ids and r["Counter_Name"] == ctr]
+            c[ctr] = statistics.mean(v) if v else float("nan")
+        gui = c["GRBM_GUI_ACTIVE"] / 8
+        waves = c["SQ_WAVES"]
+        issue_us = c["SQ_INSTS_VALU"] / (256 * 4 * 2.4e9 / 4) * 1e6
+        us = achieved.get(key)
+        per = CHUNKS if key == "smallblock_reduce_chunk" else 1
+        meas = f"{us / per:.2f}" + (" (step / 8)" if per > 1 else "") if us else "—"
+        lines.append(f"| {what} | {waves:,.0f} | {c['SQ_INSTS_VALU'] / waves:.0f} | "
+                     f"{c['SQ_INSTS_VMEM_RD'] / waves:.0f} / {c['SQ_INSTS_VMEM_WR'] / waves:.0f} | {gui:,.0f} | "
+                     f"{100 * c['SQ_ACTIVE_INST_VALU'] / 256 / gui:.0f}% | "
+                     f"{4 * c['SQ_WAVE_CYCLES'] / gui / 256:.1f} | {100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.0f}% | "
+                     f"{issue_us:.2f} | {meas} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def main() -> int:
@@ -390,7 +615,9 @@ def main() -> int:
     args = parse()
     PREHEAT_MS = args.preheat_ms
     if args.summarize_counters:
-        return summarize_counters(args.summarize_counters)
+        return summarize_counters(args.summarize_counters, bench_json=args.bench_json)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.steps, bench_json=args.bench_json)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} "
@@ -679,6 +906,18 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
     gen_s = time.time() - t0
     host_x = [x.cpu().numpy() for x in xs] if not args.no_cpu_baseline else None
     input_sha = [synth.sha256(h)[:16] for h in host_x] if host_x is not None else None
+    quant = None
+    if not args.no_extras:
+        # the quantize of one rank's fp32 buffer (A2-A4 on this workload), over the 16 inputs in turn
+        qc = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(2)]
+        qs = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(2)]
+
+        def fq(i):
+            qar.qar_quantize_blocks(xs[i % N], B, qc[i % 2], qs[i % 2], stream=main_st)
+        with torch.cuda.stream(main_st):
+            quant = _rate(4 * n + qbytes, _loop_us(torch, fq, N, 48, with_min=True))
+        quant["what"] = f"qar_quantize_blocks of one rank ({n:,} fp32, block {B}), the 16 ranks in turn"
+        del qc, qs
     del xs
     nsets = 2                                   # 2 x 1.21 GB
     sets = []
@@ -794,6 +1033,7 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
     }
     if not args.no_extras:
         result["chunk_sweep"] = chunk_sweep(qar, torch, sets, B, N, n, qbytes, main_st, sides)
+        result["smallblock_quantize"] = quant
     if host_x is not None:
         gpu_c, gpu_s = sets[0]["co"].cpu().numpy(), sets[0]["so"].cpu().numpy()
         del sets
@@ -1476,6 +1716,12 @@ def ring_bench(qar, torch, np, synth, dev):
     res = _rate(2 * (n + 4 * nb) + 2 * n, _loop_us(torch, fn, S, 200, warmup=5, with_min=True))
     res["graph_replay"] = _rate(2 * (n + 4 * nb) + 2 * n, _graph_loop_us(torch, fn, S, reps=4))
     res["workload"] = w.description
+
+    def fq(i):
+        c, s, l, co, so = sets[i]
+        qar.qar_quantize_blocks(l, B, co, so)
+    res["quantize"] = _rate(2 * n + n + 4 * nb, _graph_loop_us(torch, fq, S, reps=4))
+    res["quantize"]["what"] = "quantize of one rank's [2048, 3840] bf16 buffer, 32 calls per HIP graph replay"
     res["error_per_step"] = ring_errors(qar, torch, np, host, B, dev)
     return res
 
