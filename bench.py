@@ -1328,6 +1328,25 @@ def _loop_us(torch, fn, count, reps, warmup=3, with_min=False):
     return _segmented_us(torch, lambda i: fn(i % count), reps, with_min=with_min)
 
 
+def copy_reference_graph(torch, nbytes, count, dev):
+    """The same plain device copy as copy_reference, with as many rotated
+    buffer pairs as the kernel it stands beside and timed the same way (the
+    calls captured in one HIP graph, replayed back to back): for kernels of a
+    few microseconds, where the per-call host work would set the pace."""
+    half = (nbytes // 2) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(count)]
+
+    def fn(i):
+        src, dst = pairs[i]
+        dst.copy_(src)
+    r = _rate(2 * half, _graph_loop_us(torch, fn, count, reps=4))
+    r["what"] = (f"torch copy_ of {half:,} bytes ({2 * half:,} HBM bytes moved, as the kernel beside it), "
+                 f"{count} rotated buffer pairs, {count} calls per HIP graph replay")
+    del pairs
+    return r
+
+
 def _graph_of(torch, fn):
     """fn() captured in a HIP graph (torch.cuda.graph), after one eager call
     that creates the library's cached events."""
@@ -1722,6 +1741,9 @@ def ring_bench(qar, torch, np, synth, dev):
         qar.qar_quantize_blocks(l, B, co, so)
     res["quantize"] = _rate(2 * n + n + 4 * nb, _graph_loop_us(torch, fq, S, reps=4))
     res["quantize"]["what"] = "quantize of one rank's [2048, 3840] bf16 buffer, 32 calls per HIP graph replay"
+    res["copy_same_bytes"] = copy_reference_graph(torch, res["graph_replay"]["algorithmic_bytes"], S, dev)
+    res["copy_same_bytes"]["copy_time_over_step_time"] = round(
+        res["copy_same_bytes"]["avg_us"] / res["graph_replay"]["avg_us"], 4)
     res["error_per_step"] = ring_errors(qar, torch, np, host, B, dev)
     return res
 

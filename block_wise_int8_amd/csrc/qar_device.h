@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace qar {
 
 constexpr int kLaneElems = 16;
@@ -48,6 +50,22 @@ __device__ __forceinline__ void store_b64(void* p, uint2 q) {
     __builtin_nontemporal_store(v, reinterpret_cast<qar_u32x2*>(p));
 }
 
+__device__ __forceinline__ uint32_t load_b32(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+__device__ __forceinline__ void store_b32(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+
+__device__ __forceinline__ uint32_t load_b16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+
+__device__ __forceinline__ void store_b16(void* p, uint32_t v) {
+    __builtin_nontemporal_store((uint16_t)v, reinterpret_cast<uint16_t*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // tile order across the chip's eight XCDs
 //
@@ -74,15 +92,26 @@ constexpr int kDppSwapPairs = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
 
+// Max over each aligned group of L lanes (4 .. 64); every lane of a group
+// gets its group's max.  Up to 16 lanes the groups lie inside one DPP row;
+// 32 and 64 lanes add cross-row exchanges.
+template <int L>
+__device__ __forceinline__ float lanes_max(float m) {
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "lane group");
+    m = fmaxf(m, dpp_move<kDppSwapAdjacent>(m));
+    m = fmaxf(m, dpp_move<kDppSwapPairs>(m));
+    if constexpr (L >= 8) m = fmaxf(m, dpp_move<kDppRowHalfMirror>(m));
+    if constexpr (L >= 16) m = fmaxf(m, dpp_move<kDppRowMirror>(m));
+    if constexpr (L >= 32) m = fmaxf(m, __shfl_xor(m, 16));
+    if constexpr (L >= 64) m = fmaxf(m, __shfl_xor(m, 32));
+    return m;
+}
+
 // Max over the B/16 lanes of one block; every lane of the block gets it.
 template <int B>
 __device__ __forceinline__ float block_max(float m) {
     static_assert(B == 64 || B == 128 || B == 256, "block size");
-    m = fmaxf(m, dpp_move<kDppSwapAdjacent>(m));
-    m = fmaxf(m, dpp_move<kDppSwapPairs>(m));
-    if constexpr (B >= 128) m = fmaxf(m, dpp_move<kDppRowHalfMirror>(m));
-    if constexpr (B >= 256) m = fmaxf(m, dpp_move<kDppRowMirror>(m));
-    return m;
+    return lanes_max<B / kLaneElems>(m);
 }
 
 // ---------------------------------------------------------------------------
@@ -159,6 +188,25 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
 
 // Codes of v[0..15] for scale s; all zero when s == 0.  w[i] receives the
 // code of v[i] in its low byte (and 1.5 * 2^23 + code as a float).
+// Code bits of P values for an integer code format with largest code Q
+// (as quantize16 below, for any count): w[i] holds 1.5 * 2^23 + code_i as a
+// float, its low bits the code in two's complement.
+template <int P>
+__device__ __forceinline__ void int_code_words(const float (&v)[P], float s, float q, uint32_t (&w)[P]) {
+    if (s >= kFastQuotientMinScale) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < P; ++i) w[i] = code_bits_of(fast_quotient(v[i], s, r));
+    } else if (s != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(v[i] / s, -q, q) + kRoundMagic);
+    } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) w[i] = __builtin_bit_cast(uint32_t, kRoundMagic);
+    }
+}
+
 __device__ __forceinline__ uint4 quantize16(const float (&v)[kLaneElems], float s,
                                             uint32_t (&w)[kLaneElems]) {
     if (s >= kFastQuotientMinScale) {
@@ -246,6 +294,40 @@ struct Int8Codes {
 #pragma unroll
         for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
     }
+    // P = 8 or 4 consecutive codes from element e (a multiple of P): 8 or 4
+    // bytes, for the kernels whose lanes own P-element slots of data
+    template <int P>
+    using Pack = std::conditional_t<P == 8, uint2, uint32_t>;
+    template <int P>
+    static __device__ __forceinline__ Pack<P> load_p(const int8_t* c, size_t e) {
+        if constexpr (P == 8) return load_b64(c + e);
+        else return load_b32(c + e);
+    }
+    template <int P>
+    static __device__ __forceinline__ void store_p(int8_t* c, size_t e, Pack<P> q) {
+        if constexpr (P == 8) store_b64(c + e, q);
+        else store_b32(c + e, q);
+    }
+    template <int P>
+    static __device__ __forceinline__ Pack<P> quantize_p(const float (&v)[P], float s) {
+        uint32_t w[P];
+        int_code_words<P>(v, s, kQmax, w);
+        if constexpr (P == 8) return make_uint2(pack4(w[0], w[1], w[2], w[3]), pack4(w[4], w[5], w[6], w[7]));
+        else return pack4(w[0], w[1], w[2], w[3]);
+    }
+    template <int P>
+    static __device__ __forceinline__ void dequantize_p(Pack<P> q, float s, float (&y)[P]) {
+        if constexpr (P == 8) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[k] = value(q.x, k) * s;
+                y[4 + k] = value(q.y, k) * s;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = value(q, k) * s;
+        }
+    }
 };
 
 // FP8 E4M3 in the OCP format (bias 7, 3 mantissa bits, no infinity, largest
@@ -283,23 +365,27 @@ struct E4M3Codes {
         w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
         return (uint32_t)w;
     }
-    static __device__ __forceinline__ uint4 quantize(const float (&v)[kLaneElems], float s) {
-        float t[kLaneElems];
+    // the quotients of P values, ready for conversion (s != 0)
+    template <int P>
+    static __device__ __forceinline__ void quotients(const float (&v)[P], float s, float (&t)[P]) {
         if (s >= kFastMinScale) {
             const float r = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) {
+            for (int i = 0; i < P; ++i) {
                 // x = -0 gives e = +0 and +0 + -0 = +0: put the sign back.
                 // No clamp: as for int8 (code_bits_of), a normal s bounds the
                 // rounded quotient by Q + 2^-15 here.
                 t[i] = __builtin_copysignf(fast_quotient(v[i], s, r), v[i]);
             }
-        } else if (s != 0.0f) {
-#pragma unroll
-            for (int i = 0; i < kLaneElems; ++i) t[i] = __builtin_amdgcn_fmed3f(v[i] / s, -kQmax, kQmax);
         } else {
-            return make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int i = 0; i < P; ++i) t[i] = __builtin_amdgcn_fmed3f(v[i] / s, -kQmax, kQmax);
         }
+    }
+    static __device__ __forceinline__ uint4 quantize(const float (&v)[kLaneElems], float s) {
+        if (s == 0.0f) return make_uint4(0u, 0u, 0u, 0u);
+        float t[kLaneElems];
+        quotients<kLaneElems>(v, s, t);
         uint4 q;
         q.x = pack4(t[0], t[1], t[2], t[3]);
         q.y = pack4(t[4], t[5], t[6], t[7]);
@@ -326,6 +412,40 @@ struct E4M3Codes {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(c + e);
 #pragma unroll
         for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
+    }
+    // P = 8 or 4 consecutive codes (as Int8Codes)
+    template <int P>
+    using Pack = std::conditional_t<P == 8, uint2, uint32_t>;
+    template <int P>
+    static __device__ __forceinline__ Pack<P> load_p(const int8_t* c, size_t e) {
+        if constexpr (P == 8) return load_b64(c + e);
+        else return load_b32(c + e);
+    }
+    template <int P>
+    static __device__ __forceinline__ void store_p(int8_t* c, size_t e, Pack<P> q) {
+        if constexpr (P == 8) store_b64(c + e, q);
+        else store_b32(c + e, q);
+    }
+    template <int P>
+    static __device__ __forceinline__ Pack<P> quantize_p(const float (&v)[P], float s) {
+        if (s == 0.0f) return Pack<P>{};
+        float t[P];
+        quotients<P>(v, s, t);
+        if constexpr (P == 8) return make_uint2(pack4(t[0], t[1], t[2], t[3]), pack4(t[4], t[5], t[6], t[7]));
+        else return pack4(t[0], t[1], t[2], t[3]);
+    }
+    template <int P>
+    static __device__ __forceinline__ void dequantize_p(Pack<P> q, float s, float (&y)[P]) {
+        if constexpr (P == 8) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[k] = value(q.x, k) * s;
+                y[4 + k] = value(q.y, k) * s;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] = value(q, k) * s;
+        }
     }
 };
 
@@ -432,6 +552,52 @@ struct Int4Codes {
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[k] = value(w, k) * s;
+        }
+    }
+    // P = 8 or 4 consecutive codes from element e (a multiple of P): 4 or 2
+    // bytes at e / 2, in the low bits of a word
+    template <int P>
+    using Pack = uint32_t;
+    template <int P>
+    static __device__ __forceinline__ uint32_t load_p(const int8_t* c, size_t e) {
+        if constexpr (P == 8) return load_b32(c + e / 2);
+        else return load_b16(c + e / 2);
+    }
+    template <int P>
+    static __device__ __forceinline__ void store_p(int8_t* c, size_t e, uint32_t q) {
+        if constexpr (P == 8) store_b32(c + e / 2, q);
+        else store_b16(c + e / 2, q);
+    }
+    template <int P>
+    static __device__ __forceinline__ uint32_t quantize_p(const float (&v)[P], float s) {
+        uint32_t w[P];
+        int_code_words<P>(v, s, kQmax, w);
+        uint32_t r = 0;
+#pragma unroll
+        for (int k = 0; k < P; ++k) r |= (w[k] & 0xFu) << (4 * k);
+        return r;
+    }
+    template <int P>
+    static __device__ __forceinline__ void dequantize_p(uint32_t q, float s, float (&y)[P]) {
+        if constexpr (P == 8) {
+            if (s <= 0x1p123f) {
+                dequantize8(q, s * 16.0f, y);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = value(q, k) * s;
+            }
+        } else {
+            if (s <= 0x1p123f) {
+                const float s16 = s * 16.0f;
+                const uint32_t hi = q >> 4; // codes 1 and 3 into the low nibbles of bytes 0 and 1
+                y[0] = sixteenth<0>(q) * s16;
+                y[1] = sixteenth<0>(hi) * s16;
+                y[2] = sixteenth<1>(q) * s16;
+                y[3] = sixteenth<1>(hi) * s16;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) y[k] = value(q, k) * s;
+            }
         }
     }
 };

@@ -50,12 +50,8 @@ hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, 
                                      hipStream_t st);
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
                            hipStream_t st, int code = kCodeInt8);
-// share > 0: the launch takes at most 1/share of the workgroups the device
-// holds at once (grid-stride over the tiles), so that `share` such launches
-// on different streams are resident together; 0: one workgroup per tile.
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st, int code = kCodeInt8,
-                         int share = 0);
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code = kCodeInt8);
 hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
                                   float* scales_out, void* out, int out_kind, hipStream_t st,
