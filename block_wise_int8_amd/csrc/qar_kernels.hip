@@ -1204,15 +1204,18 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
 }
 
 // The one-kernel step with 8 elements per lane from 2^23 elements on, 16
-// below.  Measured with N = 8, B = 256, bf16 in and out (µs, 16 -> 8 per
-// lane): 2M elements 6.94 -> 7.43; 4M 12.26 -> 12.47; 8M 21.0 -> 20.7;
-// 16.8M 38.5 -> 37.4 (E4M3 39.7 -> 37.6, 4-bit 29.2 -> 28.7).
+// below, for int8 and E4M3 codes.  Measured with N = 8, B = 256, bf16 in and
+// out (µs, 16 -> 8 per lane): 2M elements 6.94 -> 7.43; 4M 12.26 -> 12.47;
+// 8M 21.0 -> 20.7; 16.8M 38.5 -> 37.4 (E4M3 39.7 -> 37.6).  The 4-bit step,
+// bound by VALU issue, keeps 16 per lane: with 8 it issues 1.21 instead of
+// 0.89 VALU instructions per element (SQ counters) for 28.7-30.0 against
+// 29.1-29.2 µs.
 constexpr size_t kStep8MinElems = (size_t)1 << 23;
 
 hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
                                   float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
-    const bool eight = n >= kStep8MinElems;
+    const bool eight = n >= kStep8MinElems && code != kCodeInt4;
     const Grid g = grid_for(n);
     const uint32_t tiles8 = (uint32_t)((n + kTileElems8 - 1) / kTileElems8);
     const uint32_t blocks8 = tiles8 < kMaxGrid ? tiles8 : kMaxGrid;

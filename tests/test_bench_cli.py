@@ -65,6 +65,41 @@ def test_counter_summary_arithmetic(tmp_path):
     k5 = rec["kernels"]["smallblock_reduce_chunk"]
     assert step["hbm_bytes_per_step"] == bench.CHUNKS * (k5["hbm_read_bytes"] + k5["hbm_write_bytes"])
     assert step["kernel_source_sha256_16"] == bench.kernel_source_hash()
-    top = json.loads((out / "k_quantize_reduce_outliers_counters.json").read_text())
+    top = json.loads((out / os.path.basename(bench.counters_path("outliers"))).read_text())
     k2 = rec["kernels"]["outliers_step"]
     assert top["hbm_bytes_per_launch"] == k2["hbm_read_bytes"] + k2["hbm_write_bytes"]
+
+
+def test_kernel_trace_summary(tmp_path):
+    """The all-kernels trace table: one row per libqar kernel and launch
+    size with its dispatch count and durations; the launch size names the
+    workload (16 elements per lane, 8 for the kernels whose name ends in 8;
+    a ragged launch rounds up to whole tiles); other kernels are left out."""
+    rows = [("void qar::k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>(x)", 524288, [(0, 25000), (0, 27000)]),
+            ("void qar::k_reduce8<256, 0, qar::Int8Codes>(x)", 2097152, [(0, 30000)]),
+            ("void qar::k_quantize_reduce<128, 0, unsigned short, qar::Int8Codes, false>(x)", 256, [(0, 3000)]),
+            ("void qar::k_reduce_unquantized<unsigned short>(x)", 491520, [(0, 14000)]),
+            ("void qar::k_ring_step<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>(x)", 30720,
+             [(0, 3000)]),
+            ("__amd_rocclr_copyBuffer", 1 << 20, [(0, 9000)])]
+    d = tmp_path / "prof"
+    d.mkdir()
+    with open(d / "bench_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"])
+        w.writeheader()
+        for name, grid, spans in rows:
+            for t0, t1 in spans:
+                w.writerow({"Kernel_Name": name, "Start_Timestamp": t0, "End_Timestamp": t1, "Grid_Size_X": grid})
+    out = tmp_path / "profiles"
+    out.mkdir()
+    assert bench.summarize_kernel_trace(str(d), str(out)) == 0
+    table = [ln for ln in (out / "kernel_trace_all_kernels.md").read_text().splitlines() if ln.startswith("| ")]
+    body = {ln.split("|")[1].strip().strip("*`"): [c.strip() for c in ln.split("|")[2:-1]] for ln in table[1:]}
+    assert len(body) == 5 and not any("copyBuffer" in k for k in body)
+    head = body["k_reduce<64, -1, FlatLanes<64>, Int8Codes>"]
+    assert head[:5] == ["524,288", "8,388,608", f"small-block, {bench.CHUNKS} chunks (the headline)", "2", "26.00"]
+    assert body["k_reduce8<256, 0, Int8Codes>"][1:3] == ["16,777,216", "outliers: N=8 x 16,777,216 bf16"]
+    assert body["k_quantize_reduce<128, 0, unsigned short, Int8Codes, false>"][2] == "tiny: N=4 x 4,096 bf16"
+    assert body["k_reduce_unquantized<unsigned short>"][2].startswith("ring: N=4")
+    assert body["k_ring_step<256, unsigned short, FlatLanes<256>, Int8Codes>"][2] == \
+        "simulated all-reduce of the ring workload, 16 chunks"

@@ -1,11 +1,12 @@
 """The one-kernel step (quantize own + reduce) from 2^23 elements on, where
-the library runs its 8-elements-per-lane kernel, against the CPU oracle on
-every element: all three code formats, bf16 and fp32 inputs, every output
+the library runs its 8-elements-per-lane kernel for int8 and E4M3 codes,
+against the CPU oracle on every element: all three code formats (4-bit
+codes keep the 16-per-lane kernel), bf16 and fp32 inputs, every output
 kind, rank counts whose loads go dense (5, 8) and not (3, 9), the own rank
 first, in the middle and last, and a ragged tail (n is a multiple of the
-block but not of the 2048-element tile).  Below 2^23 the other kernel runs;
-the parity tests in test_gpu_parity.py, test_gpu_e4m3.py and
-test_gpu_int4.py cover it."""
+block but not of the 2048-element tile).  Below 2^23 the 16-per-lane kernel
+runs for every format; the parity tests in test_gpu_parity.py,
+test_gpu_e4m3.py and test_gpu_int4.py cover it."""
 import functools
 
 import numpy as np
