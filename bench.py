@@ -154,7 +154,7 @@ def counter_catalogue():
     n5c = w5.n // CHUNKS
     out.append(("smallblock_reduce_chunk", f"small-block step: one of {CHUNKS} chunks of the fused reduce "
                 f"(N={w5.nranks} x {n5c:,} fp32-derived codes, B=64, no out)",
-                "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>", grid(n5c), w5.nranks * qb(n5c, 64),
+                "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes, 16>", grid(n5c), w5.nranks * qb(n5c, 64),
                 qb(n5c, 64)))
     out.append(("smallblock_quantize", f"small-block quantize (one rank: {w5.n:,} fp32, B=64)",
                 "k_quantize_slots<64, float, qar::Int8Codes>", grid(w5.n), 4 * w5.n, qb(w5.n, 64)))
@@ -180,7 +180,7 @@ def counter_catalogue():
                 "k_quantize_reduce8<256, 0, unsigned short, qar::E4M3Codes, true>", grid8(n2),
                 2 * n2 + (N2 - 1) * qb(n2, 256), 2 * qb(n2, 256) + 2 * n2))
     out.append(("outliers_reduce_int4", "outlier fused reduce, 4-bit codes, no out",
-                "k_reduce<256, -1, qar::FlatLanes<256>, qar::Int4Codes>", grid(n2), N2 * qb(n2, 256, 2),
+                "k_reduce<256, -1, qar::FlatLanes<256>, qar::Int4Codes, 8>", grid(n2), N2 * qb(n2, 256, 2),
                 qb(n2, 256, 2)))
     out.append(("outliers_step_int4", "outlier one-kernel step, 4-bit codes",
                 "k_quantize_reduce<256, 0, unsigned short, qar::Int4Codes, true>", grid(n2),
@@ -411,7 +411,7 @@ def summarize_trace(d: str, steps: int, out_dir: str = PROFILES, bench_json: str
     dbs = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
     if not dbs:
         raise SystemExit(f"no rocprofv3 database under {d}")
-    name = "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>"
+    name = "k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes, 16>"
     con = sqlite3.connect(dbs[0])
     rows = [r for r in con.execute("select name, start, end, queue_id, grid_x from kernels order by start")
             if name in r[0]]

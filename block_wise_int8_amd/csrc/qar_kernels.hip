@@ -307,12 +307,19 @@ __device__ __align__(64) uint32_t g_unused_slot[16];
 // load, so with 1-4 ranks in the last group (N = 2: 16% slower) the loads
 // branch around the unused slots instead; the launcher picks by N.  The
 // plain reduce always branches (the dense form measured 4% slower there).
-template <int B, int OUT, typename Lanes, typename OwnIn, typename C, bool kDense = false>
+//
+// G ranks' loads are in flight together, one group after another.  The
+// plain reduce without output takes G = 16 from 9 ranks on (N = 16 × 67M,
+// B = 64: 207.9 -> 199.3 µs as one launch, 203.2 -> 199.1 µs in 8 chunks
+// over 4 streams; 124 VGPRs instead of 78, still 4 waves per SIMD).  With a
+// fused output G = 16 needs 131-142 VGPRs (3 waves per SIMD), unmeasured, so
+// those keep 8, and so does the step, whose own rank's registers would not
+// leave room for 16.
+template <int B, int OUT, typename Lanes, typename OwnIn, typename C, bool kDense = false, int G = 8>
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                              const OwnIn* __restrict__ x_own, int own,
                                              int8_t* __restrict__ own_codes, float* __restrict__ own_scales) {
-    constexpr int G = 8; // ranks whose loads are in flight together
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
     using Vec = typename C::Vec;
@@ -412,12 +419,12 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
     }
 }
 
-template <int B, int OUT, typename Lanes, typename C = Int8Codes>
+template <int B, int OUT, typename Lanes, typename C = Int8Codes, int G = 8>
 __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
                                                      int8_t* codes_out, float* scales_out,
                                                      void* __restrict__ out, uint32_t ntiles) {
-    reduce_tiles<B, OUT, Lanes, void, C>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr, -1,
-                                         nullptr, nullptr);
+    reduce_tiles<B, OUT, Lanes, void, C, false, G>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr,
+                                                   -1, nullptr, nullptr);
 }
 
 template <int B, int OUT, typename In, typename C = Int8Codes, bool kDense = true>
@@ -1196,6 +1203,9 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
                     return launch(k_reduce8<B, OUT, C>, blocks, st, rp, nranks, n, codes_out, scales_out, out, tiles);
                 }
                 const Grid g = grid_for(n);
+                if (OUT == kOutNone && nranks > kMaxRanks8)
+                    return launch(k_reduce<B, kOutNone, FlatLanes<B>, C, 16>, g.blocks, st, rp, nranks,
+                                  FlatLanes<B>{n}, codes_out, scales_out, out, g.ntiles);
                 return launch(k_reduce<B, OUT, FlatLanes<B>, C>, g.blocks, st, rp, nranks, FlatLanes<B>{n},
                               codes_out, scales_out, out, g.ntiles);
             });

@@ -75,7 +75,7 @@ def test_kernel_trace_summary(tmp_path):
     size with its dispatch count and durations; the launch size names the
     workload (16 elements per lane, 8 for the kernels whose name ends in 8;
     a ragged launch rounds up to whole tiles); other kernels are left out."""
-    rows = [("void qar::k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes>(x)", 524288, [(0, 25000), (0, 27000)]),
+    rows = [("void qar::k_reduce<64, -1, qar::FlatLanes<64>, qar::Int8Codes, 16>(x)", 524288, [(0, 25000), (0, 27000)]),
             ("void qar::k_reduce8<256, 0, qar::Int8Codes>(x)", 2097152, [(0, 30000)]),
             ("void qar::k_quantize_reduce<128, 0, unsigned short, qar::Int8Codes, false>(x)", 256, [(0, 3000)]),
             ("void qar::k_reduce_unquantized<unsigned short>(x)", 491520, [(0, 14000)]),
@@ -96,7 +96,7 @@ def test_kernel_trace_summary(tmp_path):
     table = [ln for ln in (out / "kernel_trace_all_kernels.md").read_text().splitlines() if ln.startswith("| ")]
     body = {ln.split("|")[1].strip().strip("*`"): [c.strip() for c in ln.split("|")[2:-1]] for ln in table[1:]}
     assert len(body) == 5 and not any("copyBuffer" in k for k in body)
-    head = body["k_reduce<64, -1, FlatLanes<64>, Int8Codes>"]
+    head = body["k_reduce<64, -1, FlatLanes<64>, Int8Codes, 16>"]
     assert head[:5] == ["524,288", "8,388,608", f"small-block, {bench.CHUNKS} chunks (the headline)", "2", "26.00"]
     assert body["k_reduce8<256, 0, Int8Codes>"][1:3] == ["16,777,216", "outliers: N=8 x 16,777,216 bf16"]
     assert body["k_quantize_reduce<128, 0, unsigned short, Int8Codes, false>"][2] == "tiny: N=4 x 4,096 bf16"
