@@ -41,11 +41,48 @@ KERNEL_SOURCES = [os.path.join(ROOT, "block_wise_int8_amd", "csrc", f)
                   for f in ("qar_kernels.hip", "qar_device.h")]
 
 
+def code_without_comments(text: str) -> str:
+    """C++ source with its comments removed and every run of blanks and
+    line breaks outside string and character literals turned into one
+    space: what the compiler sees, so that editing a comment or the layout
+    leaves the kernel hash alone."""
+    out, i, n = [], 0, len(text)
+
+    def blank():
+        if out and out[-1] != " ":
+            out.append(" ")
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            blank()
+            i = n if j < 0 else j + 2
+        elif c.isspace():
+            blank()
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out).strip()
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments left out), recorded with
+    the counter summaries: a summary whose hash differs was taken on other
+    kernels."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_without_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

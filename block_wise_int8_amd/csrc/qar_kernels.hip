@@ -312,9 +312,10 @@ __device__ __align__(64) uint32_t g_unused_slot[16];
 // plain reduce without output takes G = 16 from 9 ranks on (N = 16 × 67M,
 // B = 64: 207.9 -> 199.3 µs as one launch, 203.2 -> 199.1 µs in 8 chunks
 // over 4 streams; 124 VGPRs instead of 78, still 4 waves per SIMD).  With a
-// fused output G = 16 needs 131-142 VGPRs (3 waves per SIMD), unmeasured, so
-// those keep 8, and so does the step, whose own rank's registers would not
-// leave room for 16.
+// fused output G = 16 needs 131-142 VGPRs and the step 157 (3 waves per
+// SIMD); on 16.8M bf16, B = 256, with bf16 output (µs, G = 8 -> 16): reduce
+// N = 16 54.8 -> 54.5, N = 32 102.4 -> 104.9; step N = 16 59.9 -> 59.7,
+// N = 32 109.0 -> 110.0.  So those keep 8.
 template <int B, int OUT, typename Lanes, typename OwnIn, typename C, bool kDense = false, int G = 8>
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,

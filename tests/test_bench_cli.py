@@ -103,3 +103,17 @@ def test_kernel_trace_summary(tmp_path):
     assert body["k_reduce_unquantized<unsigned short>"][2].startswith("ring: N=4")
     assert body["k_ring_step<256, unsigned short, FlatLanes<256>, Int8Codes>"][2] == \
         "simulated all-reduce of the ring workload, 16 chunks"
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The counter summaries record a hash of the kernel code: editing a
+    comment or a blank line keeps it, editing code (also inside a string
+    literal, or a // inside one) changes it."""
+    base = 'int f(int x) { // one\n  /* two\n three */ return x + 1; }\nconst char* s = "a // b";\n'
+    same = ['int f(int x) { // other words\n  /* changed */ return x + 1; }\n\nconst char* s = "a // b";   \n',
+            'int f(int x) {\n  return x + 1; }\nconst char* s = "a // b";\n']
+    other = ['int f(int x) { // one\n  /* two */ return x + 2; }\nconst char* s = "a // b";\n',
+             'int f(int x) { return x + 1; }\nconst char* s = "a // c";\n']
+    h = bench.code_without_comments
+    assert all(h(t) == h(base) for t in same)
+    assert all(h(t) != h(base) for t in other)
