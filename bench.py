@@ -521,10 +521,10 @@ _BENCH_TIMES = {
     "smallblock_reduce_chunk": (("roofline", "step_us"),),
     "smallblock_quantize": (("smallblock_quantize", "avg_us"),),
     "outliers_step": (("outliers_step", "kernels", "k_quantize_reduce (the step)", "avg_us"),),
-    "outliers_quantize": (("outliers_step", "kernels", "k_quantize", "avg_us"),),
+    "outliers_quantize": (("outliers_step", "kernels", "k_quantize", "graph_replay", "avg_us"),),
     "outliers_reduce": (("reduce_only", "avg_us"),),
     "outliers_reduce_bf16": (("outliers_step", "kernels", "k_reduce (bf16 out)", "avg_us"),),
-    "outliers_dequantize": (("dequantize", "avg_us"),),
+    "outliers_dequantize": (("dequantize", "graph_replay", "avg_us"),),
     "outliers_comparator": (("unquantized_comparator", "avg_us"),),
     "outliers_reduce_e4m3": (("code_formats", "timing_outliers", "e4m3", "reduce_no_out", "avg_us"),),
     "outliers_step_e4m3": (("code_formats", "timing_outliers", "e4m3", "one_kernel_step", "avg_us"),),
@@ -671,7 +671,9 @@ def _write_traffic_md(path, rec, achieved, bench_json):
         "",
         "Achieved: algorithmic bytes over the kernel's time per launch in the bench.py run named above (median",
         "of event-bracketed segments of back-to-back launches over rotated sets, behind 50 ms of the same",
-        "launches; the small-block chunk: the step's 8 launches over the step's time).",
+        "launches; the small-block chunk: the step's 8 launches over the step's time; the ring step, the",
+        "ring and outlier quantizes and the dequantize, short enough for the binding's host work to set the",
+        "pace of eager calls, as HIP graph replays).",
         "",
         "| kernel | what | read (calibrated) | written | algorithmic read | algorithmic write | traffic / algorithmic"
         " | us per launch | achieved TB/s | % of 8 TB/s |",

@@ -1181,13 +1181,21 @@ hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8
 }
 
 // The reduce with 8 elements per lane (reduce_tiles8) for int8 and E4M3
-// codes from up to 8 ranks; 16 per lane for more ranks and for 4-bit codes.
-// Measured with N = 8, B = 256 (µs, 16 -> 8 per lane): 16.8M elements, no
-// output 26.8 -> 25.3, bf16 output 32.0 -> 30.6; [8192, 5376] 71.4 -> 70.0
-// and 85.3 -> 82.9; 2M elements 6.24 -> 5.62.  With N = 16 (67M elements,
-// B = 64) twice the load instructions per byte cost more than they give: 8
-// chunks over 4 streams 202.9 -> 210.1.  4-bit codes (4 bytes per lane):
-// 17.8 -> 21.0 at 16.8M elements.
+// codes from 6 to 8 ranks, and from 4 with a fused output; 16 per lane for
+// fewer ranks, for more, and for 4-bit codes.  Measured with B = 256, one
+// launch per call, µs (16 -> 8 per lane), no output / bf16 output:
+//   16.8M elements: N=1 9.7 -> 12.9 / 14.6 -> 17.3; N=3 14.0 -> 16.1 /
+//     19.6 -> 19.8; N=4 16.1 -> 17.4 / 22.0 -> 21.6; N=6 21.3 -> 21.1 /
+//     26.8 -> 26.1; N=8 26.7 -> 26.1 / 32.8 -> 31.6
+//   8.4M: N=4 9.95 -> 10.54 / 13.47 -> 12.84; N=6 12.72 -> 12.46 / 15.75 ->
+//     15.12; N=8 15.59 -> 15.12 / 18.33 -> 18.02
+//   4.2M: N=6 8.12 -> 8.65 / 9.58 -> 9.97; N=8 9.96 -> 9.87 / 11.39 -> 11.43
+//   2.1M: N=4 5.15 -> 4.83 / 5.24 -> 5.03; N=8 6.73 -> 6.08 / 6.90 -> 6.34
+// Few ranks leave too little arithmetic per element to pay for the lane's
+// fixed work twice as often.  With N = 16 (67M elements, B = 64) twice the
+// load instructions per byte cost more than they give: 8 chunks over 4
+// streams 202.9 -> 210.1.  4-bit codes (4 bytes per lane): 17.8 -> 21.0 at
+// 16.8M elements.
 constexpr int kMaxRanks8 = 8;
 
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
@@ -1198,7 +1206,8 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
             constexpr int B = decltype(bc)::value;
             return dispatch_out(out_kind, [&](auto oc) {
                 constexpr int OUT = decltype(oc)::value;
-                if (!std::is_same<C, Int4Codes>::value && nranks <= kMaxRanks8) {
+                if (!std::is_same<C, Int4Codes>::value && nranks <= kMaxRanks8 &&
+                    (nranks >= 6 || (OUT != kOutNone && nranks >= 4))) {
                     const uint32_t tiles = (uint32_t)((n + kTileElems8 - 1) / kTileElems8);
                     const uint32_t blocks = tiles < kMaxGrid ? tiles : kMaxGrid;
                     return launch(k_reduce8<B, OUT, C>, blocks, st, rp, nranks, n, codes_out, scales_out, out, tiles);
