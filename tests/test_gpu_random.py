@@ -60,19 +60,26 @@ def test_random_configuration(oracle_lib, case):
     _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own)
 
 
-@pytest.mark.parametrize("size", ["one block", "tile minus a block", "one tile", "tile plus a block"])
+EDGE_SIZES = {"one block": lambda b: b, "half tile minus a block": lambda b: 2048 - b, "half tile": lambda b: 2048,
+              "half tile plus a block": lambda b: 2048 + b, "tile minus a block": lambda b: 4096 - b,
+              "one tile": lambda b: 4096, "tile plus a block": lambda b: 4096 + b}
+
+
+@pytest.mark.parametrize("nranks", [3, 6])
+@pytest.mark.parametrize("size", list(EDGE_SIZES))
 @pytest.mark.parametrize("block", [64, 128, 256])
 @pytest.mark.parametrize("codes_fmt", ["int8", "e4m3", "int4"])
-def test_edge_sizes(oracle_lib, codes_fmt, block, size):
-    """Sizes at the edges of the tiling: a single block (one lane group of a
-    wave), one block short of a 4,096-element tile, exactly one tile, and one
-    block into a second tile, through every flat call."""
-    n = {"one block": block, "tile minus a block": 4096 - block, "one tile": 4096,
-         "tile plus a block": 4096 + block}[size]
-    rng = np.random.default_rng(20_000 + n + block)
+def test_edge_sizes(oracle_lib, codes_fmt, block, size, nranks):
+    """Sizes at the edges of the tiling, through every flat call: a single
+    block (one lane group of a wave), one block either side of and exactly a
+    2,048-element tile (the kernels with 8 elements per lane, which the reduce
+    takes from 6 ranks on for int8 and E4M3 codes) and a 4,096-element tile
+    (16 per lane)."""
+    n = EDGE_SIZES[size](block)
+    rng = np.random.default_rng(20_000 + n + block + 7 * nranks)
     dtype = "bf16" if (n // block) % 2 else "f32"
-    say(f"edge size: {codes_fmt} B={block} n={n} {dtype}")
-    _run_case(oracle_lib, rng, block, 3, dtype, n, codes_fmt, 1)
+    say(f"edge size: {codes_fmt} N={nranks} B={block} n={n} {dtype}")
+    _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, 1)
 
 
 def _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own):
