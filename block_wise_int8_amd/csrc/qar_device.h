@@ -78,6 +78,15 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t G) {
     return x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
+// The same with super-tiles of S consecutive tiles dealt round-robin to the
+// XCDs (S = 0: the contiguous ranges above).  A bijection of [0, G) when
+// G % (8 S) == 0, which the launcher guarantees before it passes S > 0.
+__device__ __forceinline__ uint32_t xcd_super_tile(uint32_t b, uint32_t G, uint32_t S) {
+    if (S == 0) return xcd_tile(b, G);
+    const uint32_t x = b % 8, l = b / 8;
+    return ((l / S) * 8 + x) * S + l % S;
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane absmax inside a block (DPP row operations, all lanes active)
 

@@ -320,13 +320,14 @@ template <int B, int OUT, typename Lanes, typename OwnIn, typename C, bool kDens
 __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                              const OwnIn* __restrict__ x_own, int own,
-                                             int8_t* __restrict__ own_codes, float* __restrict__ own_scales) {
+                                             int8_t* __restrict__ own_codes, float* __restrict__ own_scales,
+                                             uint32_t super) {
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
     using Vec = typename C::Vec;
     __shared__ Vec lds_codes[kStaged ? kThreads : 1];
     __shared__ float lds_scales[kStaged ? kThreads * kLaneElems / B : 1];
-    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_super_tile(blockIdx.x, gridDim.x, super); tile < ntiles; tile += gridDim.x) {
         const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
         const size_t ld = a.valid ? a.e0 : 0;
         const size_t blk = a.valid ? a.blk : 0;
@@ -423,9 +424,9 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
 template <int B, int OUT, typename Lanes, typename C = Int8Codes, int G = 8>
 __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
                                                      int8_t* codes_out, float* scales_out,
-                                                     void* __restrict__ out, uint32_t ntiles) {
+                                                     void* __restrict__ out, uint32_t ntiles, uint32_t super) {
     reduce_tiles<B, OUT, Lanes, void, C, false, G>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr,
-                                                   -1, nullptr, nullptr);
+                                                   -1, nullptr, nullptr, super);
 }
 
 template <int B, int OUT, typename In, typename C = Int8Codes, bool kDense = true>
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restri
                                                               int8_t* codes_out, float* scales_out,
                                                               void* __restrict__ out, uint32_t ntiles) {
     reduce_tiles<B, OUT, FlatLanes<B>, In, C, kDense>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own,
-                                                      own, own_codes, own_scales);
+                                                      own, own_codes, own_scales, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -455,14 +456,15 @@ template <int B, int OUT, typename OwnIn, typename C, bool kDense>
 __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n, int8_t* codes_out,
                                               float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                               const OwnIn* __restrict__ x_own, int own,
-                                              int8_t* __restrict__ own_codes, float* __restrict__ own_scales) {
+                                              int8_t* __restrict__ own_codes, float* __restrict__ own_scales,
+                                              uint32_t super) {
     constexpr int G = 8; // ranks whose loads are in flight together
     constexpr int P = kLaneElems8, L = B / P;
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     using In = std::conditional_t<kOwn, OwnIn, uint16_t>;
     constexpr int kRawWords = P * (int)sizeof(In) / 16; // 16-byte words of own input per lane
     using Pack = typename C::template Pack<P>;
-    for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+    for (uint32_t tile = xcd_super_tile(blockIdx.x, gridDim.x, super); tile < ntiles; tile += gridDim.x) {
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * P;
         const bool valid = e0 < n; // n % B == 0: a block is wholly inside or outside
         const size_t ld = valid ? e0 : 0;
@@ -570,9 +572,10 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
 
 template <int B, int OUT, typename C>
 __global__ __launch_bounds__(kThreads) void k_reduce8(RankPtrs rp, int nranks, size_t n, int8_t* codes_out,
-                                                      float* scales_out, void* __restrict__ out, uint32_t ntiles) {
+                                                      float* scales_out, void* __restrict__ out, uint32_t ntiles,
+                                                      uint32_t super) {
     reduce_tiles8<B, OUT, void, C, false>(rp, nranks, n, codes_out, scales_out, out, ntiles, nullptr, -1, nullptr,
-                                          nullptr);
+                                          nullptr, super);
 }
 
 template <int B, int OUT, typename In, typename C, bool kDense>
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce8(const In* __restr
                                                                float* scales_out, void* __restrict__ out,
                                                                uint32_t ntiles) {
     reduce_tiles8<B, OUT, In, C, kDense>(rp, nranks, n, codes_out, scales_out, out, ntiles, x_own, own, own_codes,
-                                         own_scales);
+                                         own_scales, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -1028,7 +1031,7 @@ hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t*
     return dispatch_out(out_kind, [&](auto oc) {
         constexpr int OUT = decltype(oc)::value;
         return launch(k_reduce<B, OUT, Lanes, C>, g.blocks, st, rp, nranks, lanes, codes_out, scales_out, out,
-                      g.ntiles);
+                      g.ntiles, 0u);
     });
 }
 
@@ -1198,6 +1201,20 @@ hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8
 // 16.8M elements.
 constexpr int kMaxRanks8 = 8;
 
+// Super-tiles of 64 tiles dealt round-robin to the XCDs instead of one range
+// per XCD, for reduces of at least 8 ranks over at least 2^25 elements.
+// Probe, rank buffers in one allocation, µs (ranges -> super-tiles): N=8
+// 44M 70.2 -> 64.2, 50M 74.8 -> 72.2; N=16 (B=256) 44M 132.0 -> 122.5;
+// N=16 (B=64) 33.5M 99.6 -> 95.0, 67M 197.0 -> 189.3.  Smaller grids and
+// fewer ranks do not gain: N=8 16.8M 26.0 -> 27.5, N=2 44M 25.5 -> 27.8,
+// N=4 67M 57.0 -> 57.6, the 8.4M chunks of the small-block headline 199
+// -> 205.  The chip's mapping of addresses to HBM channels is undocumented;
+// this follows the measurements.
+uint32_t reduce_super(int nranks, size_t n, uint32_t blocks) {
+    constexpr uint32_t kSuper = 64;
+    return nranks >= 8 && n >= ((size_t)1 << 25) && blocks % (8 * kSuper) == 0 ? kSuper : 0;
+}
+
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
                          float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
     return dispatch_code(code, [&](auto ct) {
@@ -1210,14 +1227,16 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
                     (nranks >= 6 || (OUT != kOutNone && nranks >= 4))) {
                     const uint32_t tiles = (uint32_t)((n + kTileElems8 - 1) / kTileElems8);
                     const uint32_t blocks = tiles < kMaxGrid ? tiles : kMaxGrid;
-                    return launch(k_reduce8<B, OUT, C>, blocks, st, rp, nranks, n, codes_out, scales_out, out, tiles);
+                    return launch(k_reduce8<B, OUT, C>, blocks, st, rp, nranks, n, codes_out, scales_out, out, tiles,
+                                  reduce_super(nranks, n, blocks));
                 }
                 const Grid g = grid_for(n);
+                const uint32_t super = reduce_super(nranks, n, g.blocks);
                 if (OUT == kOutNone && nranks > kMaxRanks8)
                     return launch(k_reduce<B, kOutNone, FlatLanes<B>, C, 16>, g.blocks, st, rp, nranks,
-                                  FlatLanes<B>{n}, codes_out, scales_out, out, g.ntiles);
+                                  FlatLanes<B>{n}, codes_out, scales_out, out, g.ntiles, super);
                 return launch(k_reduce<B, OUT, FlatLanes<B>, C>, g.blocks, st, rp, nranks, FlatLanes<B>{n},
-                              codes_out, scales_out, out, g.ntiles);
+                              codes_out, scales_out, out, g.ntiles, super);
             });
         });
     });
