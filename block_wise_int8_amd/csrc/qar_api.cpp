@@ -14,6 +14,7 @@
 #include "qar_launch.h"
 
 static_assert(QAR_MAX_RANKS == qar::kMaxRanks, "rank limit mismatch");
+static_assert(QAR_CHUNK_RUN_ELEMS == qar::kChunkRunElems, "the header states the run length");
 static_assert(QAR_STATIC_WORKSPACE_BYTES == qar::kStaticWorkspaceBytes, "static workspace size mismatch");
 
 namespace {
@@ -349,34 +350,32 @@ qar_status qar_quantize_reduce_int4(const void* x_own, qar_dtype dtype, uint32_t
 
 namespace {
 
-// Chunk c of the reduce (block-aligned, equal but for the last) on
-// streams[c % used], each behind whatever its stream already holds.
+// The reduce as `nchunks` interleaved chunks (clipped to the number of runs
+// of qar::kChunkRunElems elements): chunk c computes runs c, c + nchunks,
+// ..., enqueued on streams[c % used] behind whatever that stream holds.
+// Interleaved rather than contiguous chunks keep the chunks that run at
+// once reading neighbouring addresses: on the small-block workload (N = 16
+// × 67M, B = 64, 8 chunks over 4 streams) 200.5 -> 193.9 µs per step in a
+// probe, contiguous chunks against interleaved ones in runs of 2^18
+// elements, bit-identical.
 hipError_t chunks_run(const int8_t* const* codes, const float* const* scales, uint32_t nranks, size_t n,
                       uint32_t block, int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
                       uint32_t nchunks, void* const* streams, uint32_t used) {
-    const size_t nb = n / block;
-    const size_t chunks = nchunks < nb ? nchunks : nb;
-    const size_t per = (nb + chunks - 1) / chunks; // blocks per chunk
+    const size_t runs = qar::chunk_runs(n);
+    const uint32_t chunks = (uint32_t)(nchunks < runs ? nchunks : runs);
     const int kind = out_kind(out, out_dtype);
-    const size_t out_bytes = out ? dtype_bytes(out_dtype) : 0;
+    qar::RankPtrs rp;
+    fill_ranks(rp, codes, scales, nranks, 0, 0);
     hipError_t e = hipSuccess;
-    for (size_t c = 0; e == hipSuccess && c < chunks; ++c) {
-        const size_t b0 = c * per;
-        if (b0 >= nb) break;
-        const size_t bn = (nb - b0 < per) ? nb - b0 : per;
-        const size_t e0 = b0 * block;
-        qar::RankPtrs rp;
-        fill_ranks(rp, codes, scales, nranks, e0, b0);
-        void* out_c = out ? (void*)((char*)out + e0 * out_bytes) : nullptr;
-        e = qar::launch_reduce(rp, (int)nranks, bn * block, (int)block, codes_out + e0, scales_out + b0, out_c,
-                               kind, (hipStream_t)streams[c % used]);
-    }
+    for (uint32_t c = 0; e == hipSuccess && c < chunks; ++c)
+        e = qar::launch_reduce(rp, (int)nranks, n, (int)block, codes_out, scales_out, out, kind,
+                               (hipStream_t)streams[c % used], qar::kCodeInt8, qar::ChunkOf{c, chunks});
     return e;
 }
 
-uint32_t streams_used(uint32_t nchunks, size_t n, uint32_t block, uint32_t nstreams) {
-    const size_t nb = n / block;
-    const size_t chunks = nchunks < nb ? nchunks : nb;
+uint32_t streams_used(uint32_t nchunks, size_t n, uint32_t nstreams) {
+    const size_t runs = qar::chunk_runs(n);
+    const size_t chunks = nchunks < runs ? nchunks : runs;
     return (uint32_t)(chunks < nstreams ? chunks : nstreams);
 }
 
@@ -393,7 +392,7 @@ qar_status qar_reduce_quantized_chunked(const int8_t* const* codes, const float*
     if (st != QAR_OK) return st;
     if (nchunks == 0 || !streams || nstreams == 0 || nstreams > QAR_MAX_STREAMS) return QAR_ERR_INVALID_ARG;
     const hipError_t e = chunks_run(codes, scales, nranks, n, block, codes_out, scales_out, out, out_dtype, nchunks,
-                                    streams, streams_used(nchunks, n, block, nstreams));
+                                    streams, streams_used(nchunks, n, nstreams));
     return e == hipSuccess ? QAR_OK : hip_fail(e, "qar_reduce_quantized_chunked");
 }
 
@@ -409,7 +408,7 @@ qar_status qar_reduce_quantized_pipelined(const int8_t* const* codes, const floa
     // NULL (the default stream) only as the calling stream itself
     for (uint32_t i = 0; i < nstreams; ++i)
         if (!streams[i] && stream) return QAR_ERR_INVALID_ARG;
-    const uint32_t used = streams_used(nchunks, n, block, nstreams);
+    const uint32_t used = streams_used(nchunks, n, nstreams);
     ForkJoin fj((hipStream_t)stream, streams, used);
     hipError_t e = fj.fork();
     if (e == hipSuccess)

@@ -87,6 +87,21 @@ __device__ __forceinline__ uint32_t xcd_super_tile(uint32_t b, uint32_t G, uint3
     return ((l / S) * 8 + x) * S + l % S;
 }
 
+// Which tiles one launch of the reduce computes.  A whole reduce (count 1)
+// takes tiles 0 .. ntiles-1 in the XCD order above (super-tiles of `super`,
+// 0: ranges).  Chunk `chunk` of `count` interleaved chunks takes runs of q
+// consecutive tiles, runs chunk, chunk + count, ...: its local tile t is
+// tile ((t / q) count + chunk) q + t % q, taken in dispatch order.
+struct TileMap {
+    uint32_t super, chunk, count, q;
+    __device__ __forceinline__ uint32_t first(uint32_t b, uint32_t G) const {
+        return count > 1 ? b : xcd_super_tile(b, G, super);
+    }
+    __device__ __forceinline__ uint32_t tile(uint32_t t) const {
+        return count > 1 ? ((t / q) * count + chunk) * q + t % q : t;
+    }
+};
+
 // ---------------------------------------------------------------------------
 // cross-lane absmax inside a block (DPP row operations, all lanes active)
 

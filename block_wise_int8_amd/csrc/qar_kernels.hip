@@ -321,13 +321,14 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
                                              float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                              const OwnIn* __restrict__ x_own, int own,
                                              int8_t* __restrict__ own_codes, float* __restrict__ own_scales,
-                                             uint32_t super) {
+                                             TileMap map) {
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     constexpr bool kStaged = OUT != kOutNone && Lanes::kContiguous;
     using Vec = typename C::Vec;
     __shared__ Vec lds_codes[kStaged ? kThreads : 1];
     __shared__ float lds_scales[kStaged ? kThreads * kLaneElems / B : 1];
-    for (uint32_t tile = xcd_super_tile(blockIdx.x, gridDim.x, super); tile < ntiles; tile += gridDim.x) {
+    for (uint32_t t = map.first(blockIdx.x, gridDim.x); t < ntiles; t += gridDim.x) {
+        const uint32_t tile = map.tile(t);
         const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
         const size_t ld = a.valid ? a.e0 : 0;
         const size_t blk = a.valid ? a.blk : 0;
@@ -424,9 +425,9 @@ __device__ __forceinline__ void reduce_tiles(RankPtrs rp, int nranks, Lanes lane
 template <int B, int OUT, typename Lanes, typename C = Int8Codes, int G = 8>
 __global__ __launch_bounds__(kThreads) void k_reduce(RankPtrs rp, int nranks, Lanes lanes,
                                                      int8_t* codes_out, float* scales_out,
-                                                     void* __restrict__ out, uint32_t ntiles, uint32_t super) {
+                                                     void* __restrict__ out, uint32_t ntiles, TileMap map) {
     reduce_tiles<B, OUT, Lanes, void, C, false, G>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr,
-                                                   -1, nullptr, nullptr, super);
+                                                   -1, nullptr, nullptr, map);
 }
 
 template <int B, int OUT, typename In, typename C = Int8Codes, bool kDense = true>
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restri
                                                               int8_t* codes_out, float* scales_out,
                                                               void* __restrict__ out, uint32_t ntiles) {
     reduce_tiles<B, OUT, FlatLanes<B>, In, C, kDense>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, x_own,
-                                                      own, own_codes, own_scales, 0u);
+                                                      own, own_codes, own_scales, TileMap{0, 0, 1, 1});
 }
 
 // ---------------------------------------------------------------------------
@@ -457,14 +458,15 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
                                               float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                               const OwnIn* __restrict__ x_own, int own,
                                               int8_t* __restrict__ own_codes, float* __restrict__ own_scales,
-                                              uint32_t super) {
+                                              TileMap map) {
     constexpr int G = 8; // ranks whose loads are in flight together
     constexpr int P = kLaneElems8, L = B / P;
     constexpr bool kOwn = !std::is_void<OwnIn>::value;
     using In = std::conditional_t<kOwn, OwnIn, uint16_t>;
     constexpr int kRawWords = P * (int)sizeof(In) / 16; // 16-byte words of own input per lane
     using Pack = typename C::template Pack<P>;
-    for (uint32_t tile = xcd_super_tile(blockIdx.x, gridDim.x, super); tile < ntiles; tile += gridDim.x) {
+    for (uint32_t t = map.first(blockIdx.x, gridDim.x); t < ntiles; t += gridDim.x) {
+        const uint32_t tile = map.tile(t);
         const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * P;
         const bool valid = e0 < n; // n % B == 0: a block is wholly inside or outside
         const size_t ld = valid ? e0 : 0;
@@ -573,9 +575,9 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
 template <int B, int OUT, typename C>
 __global__ __launch_bounds__(kThreads) void k_reduce8(RankPtrs rp, int nranks, size_t n, int8_t* codes_out,
                                                       float* scales_out, void* __restrict__ out, uint32_t ntiles,
-                                                      uint32_t super) {
+                                                      TileMap map) {
     reduce_tiles8<B, OUT, void, C, false>(rp, nranks, n, codes_out, scales_out, out, ntiles, nullptr, -1, nullptr,
-                                          nullptr, super);
+                                          nullptr, map);
 }
 
 template <int B, int OUT, typename In, typename C, bool kDense>
@@ -585,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce8(const In* __restr
                                                                float* scales_out, void* __restrict__ out,
                                                                uint32_t ntiles) {
     reduce_tiles8<B, OUT, In, C, kDense>(rp, nranks, n, codes_out, scales_out, out, ntiles, x_own, own, own_codes,
-                                         own_scales, 0u);
+                                         own_scales, TileMap{0, 0, 1, 1});
 }
 
 // ---------------------------------------------------------------------------
@@ -1031,7 +1033,7 @@ hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t*
     return dispatch_out(out_kind, [&](auto oc) {
         constexpr int OUT = decltype(oc)::value;
         return launch(k_reduce<B, OUT, Lanes, C>, g.blocks, st, rp, nranks, lanes, codes_out, scales_out, out,
-                      g.ntiles, 0u);
+                      g.ntiles, TileMap{0, 0, 1, 1});
     });
 }
 
@@ -1215,8 +1217,34 @@ uint32_t reduce_super(int nranks, size_t n, uint32_t blocks) {
     return nranks >= 8 && n >= ((size_t)1 << 25) && blocks % (8 * kSuper) == 0 ? kSuper : 0;
 }
 
+// The launch of a reduce over n elements in tiles of tile_elems: the whole
+// of it, or one chunk of interleaved chunks (ChunkOf).  blocks == 0: this
+// chunk has no runs.
+struct ReduceGrid {
+    uint32_t ntiles, blocks;
+    TileMap map;
+};
+
+ReduceGrid reduce_grid(int nranks, size_t n, uint32_t tile_elems, ChunkOf chunk) {
+    const size_t tiles = (n + tile_elems - 1) / tile_elems;
+    ReduceGrid r;
+    if (chunk.count > 1) {
+        const uint32_t q = (uint32_t)(kChunkRunElems / tile_elems);
+        const size_t runs = (tiles + q - 1) / q;
+        const size_t mine = chunk.index < runs ? (runs - 1 - chunk.index) / chunk.count + 1 : 0;
+        r.ntiles = (uint32_t)(mine * q);
+        r.map = TileMap{0, chunk.index, chunk.count, q};
+    } else {
+        r.ntiles = (uint32_t)tiles;
+        r.map = TileMap{0, 0, 1, 1};
+    }
+    r.blocks = r.ntiles < kMaxGrid ? r.ntiles : kMaxGrid;
+    if (chunk.count <= 1) r.map.super = reduce_super(nranks, n, r.blocks);
+    return r;
+}
+
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st, int code) {
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code, ChunkOf chunk) {
     return dispatch_code(code, [&](auto ct) {
         using C = typename decltype(ct)::type;
         return dispatch_block(block, [&](auto bc) {
@@ -1225,18 +1253,18 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
                 constexpr int OUT = decltype(oc)::value;
                 if (!std::is_same<C, Int4Codes>::value && nranks <= kMaxRanks8 &&
                     (nranks >= 6 || (OUT != kOutNone && nranks >= 4))) {
-                    const uint32_t tiles = (uint32_t)((n + kTileElems8 - 1) / kTileElems8);
-                    const uint32_t blocks = tiles < kMaxGrid ? tiles : kMaxGrid;
-                    return launch(k_reduce8<B, OUT, C>, blocks, st, rp, nranks, n, codes_out, scales_out, out, tiles,
-                                  reduce_super(nranks, n, blocks));
+                    const ReduceGrid g = reduce_grid(nranks, n, kTileElems8, chunk);
+                    if (g.blocks == 0) return hipSuccess;
+                    return launch(k_reduce8<B, OUT, C>, g.blocks, st, rp, nranks, n, codes_out, scales_out, out,
+                                  g.ntiles, g.map);
                 }
-                const Grid g = grid_for(n);
-                const uint32_t super = reduce_super(nranks, n, g.blocks);
+                const ReduceGrid g = reduce_grid(nranks, n, kTileElems, chunk);
+                if (g.blocks == 0) return hipSuccess;
                 if (OUT == kOutNone && nranks > kMaxRanks8)
                     return launch(k_reduce<B, kOutNone, FlatLanes<B>, C, 16>, g.blocks, st, rp, nranks,
-                                  FlatLanes<B>{n}, codes_out, scales_out, out, g.ntiles, super);
+                                  FlatLanes<B>{n}, codes_out, scales_out, out, g.ntiles, g.map);
                 return launch(k_reduce<B, OUT, FlatLanes<B>, C>, g.blocks, st, rp, nranks, FlatLanes<B>{n},
-                              codes_out, scales_out, out, g.ntiles, super);
+                              codes_out, scales_out, out, g.ntiles, g.map);
             });
         });
     });

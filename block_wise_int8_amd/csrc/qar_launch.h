@@ -50,8 +50,21 @@ hipError_t launch_reduce_unquantized(const PlainPtrs& xp, int nranks, size_t n, 
                                      hipStream_t st);
 hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8_t* codes, float* scales,
                            hipStream_t st, int code = kCodeInt8);
+// A chunk of a reduce cut into `count` interleaved chunks: the element range
+// is taken in runs of kChunkRunElems, and chunk `index` computes runs index,
+// index + count, index + 2 count, ...  The pointers passed with it are those
+// of the whole reduce, and n is the whole reduce's element count.
+constexpr size_t kChunkRunElems = (size_t)1 << 18;
+struct ChunkOf {
+    uint32_t index, count;
+};
+// Number of runs of kChunkRunElems that n elements take (the most chunks a
+// reduce of n elements can be cut into).
+inline size_t chunk_runs(size_t n) { return (n + kChunkRunElems - 1) / kChunkRunElems; }
+
 hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, int8_t* codes_out,
-                         float* scales_out, void* out, int out_kind, hipStream_t st, int code = kCodeInt8);
+                         float* scales_out, void* out, int out_kind, hipStream_t st, int code = kCodeInt8,
+                         ChunkOf chunk = ChunkOf{0, 1});
 hipError_t launch_quantize_reduce(const void* x_own, int in_kind, int own, const RankPtrs& rp, int nranks,
                                   size_t n, int block, int8_t* own_codes, float* own_scales, int8_t* codes_out,
                                   float* scales_out, void* out, int out_kind, hipStream_t st,

@@ -23,6 +23,7 @@ QAR_SCHEDULE_ONE_SHOT, QAR_SCHEDULE_RING = 0, 1
 QAR_MAX_RANKS = 32
 QAR_MAX_STREAMS = 16
 QAR_STATIC_WORKSPACE_BYTES = 64 << 20
+QAR_CHUNK_RUN_ELEMS = 1 << 18
 BLOCK_SIZES = (64, 128, 256)
 
 _vp, _sz, _u32, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int

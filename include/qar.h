@@ -143,21 +143,27 @@ qar_status qar_quantize_reduce(const void* x_own, qar_dtype dtype, uint32_t own,
                                int8_t* codes_out, float* scales_out, void* out, qar_dtype out_dtype,
                                void* stream);
 
+/* Elements per run of the chunked calls' interleaved chunks. */
+#define QAR_CHUNK_RUN_ELEMS (1u << 18)
+
 /*
  * The same reduce as a pipeline of chunks over streams (the pages' deep
  * pipelining of communication and compute, "key innovations" item 2 and
- * "key design" item 3, taken on one GPU).  The block range is cut into
- * `nchunks` block-aligned chunks of equal size (the last one shorter), and
- * chunk c is enqueued on streams[c % nstreams] behind whatever that stream
- * already holds.  Nothing else is enqueued: no event, no wait.  The caller
+ * "key design" item 3, taken on one GPU).  The elements are taken in runs
+ * of QAR_CHUNK_RUN_ELEMS (the last run shorter; a run holds whole blocks)
+ * and cut into `nchunks` interleaved chunks: chunk c computes runs c,
+ * c + nchunks, c + 2 nchunks, ..., so the chunks that run at once read
+ * neighbouring addresses.  Chunk c is enqueued on streams[c % nstreams]
+ * behind whatever that stream already holds.  Nothing else is enqueued: no event, no wait.  The caller
  * orders the chunks after the producers of the inputs and before the
  * consumers of the outputs on every stream used (events, or by producing
  * and consuming on those streams).  Consecutive calls on the same streams
  * therefore overlap: a stream holds its chunk in flight and the next
  * call's behind it (double buffering), so one stream's kernel ramps up
- * while another's drains.  Results are bit-identical to
- * qar_reduce_quantized for every nchunks and nstreams.
- *   nchunks   >= 1 (clipped to the number of blocks).
+ * while another's drains; two calls with the same n, nchunks and streams
+ * give chunk c the same runs on the same stream.  Results are
+ * bit-identical to qar_reduce_quantized for every nchunks and nstreams.
+ *   nchunks   >= 1 (clipped to the number of runs).
  *   streams   HOST array of nstreams hipStream_t (as void*), 1 .. QAR_MAX_STREAMS;
  *             NULL (the default stream) is allowed; the first
  *             min(nchunks, nstreams) are used.
@@ -178,7 +184,7 @@ qar_status qar_reduce_quantized_chunked(const int8_t* const* codes, const float*
  * enqueued with qar_reduce_quantized_chunked between one fork and one
  * join).  The events come from a per-device pool (created on first use,
  * never device memory).  Results are bit-identical to qar_reduce_quantized.
- *   nchunks   >= 1 (clipped to the number of blocks).
+ *   nchunks   >= 1 (clipped to the number of runs of QAR_CHUNK_RUN_ELEMS).
  *   streams   HOST array of nstreams hipStream_t (as void*),
  *             1 .. QAR_MAX_STREAMS; an entry may be NULL (the default
  *             stream) only when `stream` is NULL too, i.e. when it is the

@@ -20,6 +20,21 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, name), name
 
 
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's limits and sizes."""
+    import re
+    text = open(qar.HEADER).read()
+
+    def define(name):
+        m = re.search(rf"^#define {name} ([^\n]+?)\s*$", text, re.M)
+        assert m, name
+        expr = re.sub(r"(\d)u\b", r"\1", m.group(1).replace("(size_t)", ""))
+        assert re.fullmatch(r"[\d\s()<]+", expr), expr          # integers, parentheses and shifts only
+        return eval(expr, {})
+    for name in ("QAR_MAX_RANKS", "QAR_MAX_STREAMS", "QAR_STATIC_WORKSPACE_BYTES", "QAR_CHUNK_RUN_ELEMS"):
+        assert define(name) == getattr(qar, name), name
+
+
 def test_status_strings(L):
     for s in range(6):
         assert L.qar_status_string(s)

@@ -15,6 +15,8 @@ from gpu_util import (SUM_OUTLIER, TILE, assert_same_bits16, assert_same_codes, 
 
 pytestmark = pytest.mark.gpu
 
+CHUNK_RUN = qar.QAR_CHUNK_RUN_ELEMS      # elements per run of the chunked calls' interleaved chunks
+
 
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
@@ -192,8 +194,9 @@ def test_quantize_reduce_parity(oracle_lib, nranks, own, dtype, block):
 @pytest.mark.parametrize("nstreams", [1, 4])
 @pytest.mark.parametrize("nchunks", [1, 3, 8, 16, 32, 64])
 def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
+    # chunks are interleaved runs of 2^18 elements: five and a part here
     block, nranks = 64, 5
-    n = ragged_n(block, tiles=6)
+    n = 5 * CHUNK_RUN + ragged_n(block, tiles=3)
     xs = [mixed_f32(700 + r, n, block, SUM_OUTLIER) for r in range(nranks)]
     codes, scales = _rank_codes(oracle_lib, xs, block)
     dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
@@ -208,15 +211,17 @@ def test_pipelined_bit_identical(oracle_lib, nchunks, nstreams):
     assert_same_f32(to_host(out), oracle_lib.dequantize(wc, ws, block, "f32"), "out")
 
 
+@pytest.mark.parametrize("nranks", [5, 16])
 @pytest.mark.parametrize("with_caller", [False, True])
 @pytest.mark.parametrize("nchunks,nstreams", [(1, 1), (3, 2), (8, 4), (16, 4), (5, 16)])
-def test_chunked_bit_identical(oracle_lib, nchunks, nstreams, with_caller):
-    """qar_reduce_quantized_chunked: chunk c on streams[c % S] with no event
-    of its own; the caller forks the streams off the current one, runs two
-    calls back to back (the second reusing the first's output buffers, as a
-    pipelined sequence of reduces does) and joins them."""
-    block, nranks = 64, 5
-    n = ragged_n(block, tiles=6)
+def test_chunked_bit_identical(oracle_lib, nchunks, nstreams, with_caller, nranks):
+    """qar_reduce_quantized_chunked: chunk c (runs c, c + C, ... of 2^18
+    elements) on streams[c % S] with no event of its own; the caller forks
+    the streams off the current one, runs two calls back to back (the second
+    reusing the first's output buffers, as a pipelined sequence of reduces
+    does) and joins them.  n spans five runs and a ragged part of a sixth."""
+    block = 64
+    n = 5 * CHUNK_RUN + ragged_n(block, tiles=3)
     xs = [mixed_f32(710 + r, n, block, SUM_OUTLIER) for r in range(nranks)]
     codes, scales = _rank_codes(oracle_lib, xs, block)
     dc, ds = [to_dev(c) for c in codes], [to_dev(s) for s in scales]
