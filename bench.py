@@ -1141,7 +1141,8 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
             "input_sha256_16": input_sha,
             "step": (f"one-shot fused reduce (dequantize {N} quantized contributions, fp32 sum in rank order, "
                      f"requantize; no dequantized output) as one qar_reduce_quantized_chunked call: {CHUNKS} "
-                     f"chunks over {STREAMS} streams (the caller's + {STREAMS - 1}), two chunks per stream"),
+                     f"chunks over {STREAMS} streams (the caller's + {STREAMS - 1}), two chunks per stream; "
+                     f"chunk c takes the runs c, c + {CHUNKS}, ... of {qar.QAR_CHUNK_RUN_ELEMS:,} elements"),
             "codes": f"int8 with one fp32 scale per block of {B} (arithmetic in fp32)",
             "payload": "bf16-equivalent: N * n * 2 bytes per step (the inputs are fp32; fp32 payload beside it)",
             "buffer_sets": nsets, "footprint_bytes": nsets * (N + 1) * qbytes,
