@@ -337,7 +337,8 @@ def qar_reduce_quantized_pipelined(codes: list[torch.Tensor], scales: list[torch
 def qar_reduce_quantized_chunked(codes: list[torch.Tensor], scales: list[torch.Tensor], block: int, nchunks: int,
                                  streams: list, codes_out: torch.Tensor | None = None,
                                  scales_out: torch.Tensor | None = None, out: torch.Tensor | None = None):
-    """The reduce cut into ``nchunks`` chunks, chunk c enqueued on
+    """The reduce cut into ``nchunks`` chunks (chunk c takes the runs c,
+    c + nchunks, ... of QAR_CHUNK_RUN_ELEMS elements), chunk c enqueued on
     ``streams[c % len(streams)]`` behind that stream's earlier work, with no
     event or wait: the caller orders the streams."""
     if len(codes) != len(scales) or not codes:
