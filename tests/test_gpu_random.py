@@ -1,7 +1,8 @@
 """Seeded random configurations through every flat call, int8, E4M3 and
 4-bit codes, against the oracle bit for bit: rank count, block size, input type,
-output type, size (whole blocks, from one block to several tiles) and the
-value distribution all drawn per case."""
+output type, size (whole blocks, from one block to several tiles, and for
+the chunked calls up to several interleaved runs) and the value distribution
+all drawn per case."""
 import os
 
 import numpy as np
@@ -134,6 +135,56 @@ def _run_case(oracle_lib, rng, block, nranks, dtype, n, codes_fmt, own):
     rgc, rgs = o_ring(wq[0][0], wq[0][1], xs[-1], block)
     assert_same_codes(view(gc_), rgc, "ring codes")
     assert_same_f32(to_host(gs_), rgs, "ring scales")
+
+
+
+@pytest.mark.parametrize("case", range(max(4, CASES // 8)))
+def test_random_chunked_runs(oracle_lib, case):
+    """The chunked and the pipelined reduce at sizes of zero to six runs of
+    QAR_CHUNK_RUN_ELEMS plus a ragged part, with random rank, chunk and
+    stream counts (the chunked call also with a fused output), so that the
+    interleaved chunks' whole runs, the last partial run and chunk counts
+    above the run count are all met; against the oracle."""
+    rng = np.random.default_rng(50_000 + case)
+    run = qar.QAR_CHUNK_RUN_ELEMS
+    block = int(rng.choice([64, 128, 256]))
+    nranks = int(rng.integers(1, 17))
+    n = int(rng.integers(0, 7)) * run + int(rng.integers(1, run // block)) * block
+    nchunks = int(rng.integers(1, 13))
+    nstreams = int(rng.integers(1, 5))
+    out_kind = [None, "bf16", "f32"][int(rng.integers(0, 3))]
+    say(f"random chunked case {case}: N={nranks} B={block} n={n} chunks={nchunks} streams={nstreams} out={out_kind}")
+    xs = [_draw(rng, n, block, "bf16") for _ in range(nranks)]
+    q = [oracle_lib.quantize(x, block) for x in xs]
+    dc, ds = [to_dev(c) for c, _ in q], [to_dev(s) for _, s in q]
+    cur = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    out = None if out_kind is None else torch.empty(
+        n, dtype=torch.bfloat16 if out_kind == "bf16" else torch.float32, device="cuda:0")
+    oc = torch.empty(n, dtype=torch.int8, device="cuda:0")
+    os_ = torch.empty(n // block, dtype=torch.float32, device="cuda:0")
+    fork = torch.cuda.Event()                 # the chunks run after the copies above
+    fork.record(cur)
+    for st in streams:
+        st.wait_event(fork)
+    qar.qar_reduce_quantized_chunked(dc, ds, block, nchunks, streams, oc, os_, out=out)
+    for st in streams:
+        done = torch.cuda.Event()
+        done.record(st)
+        cur.wait_event(done)
+    torch.cuda.synchronize()
+    rc, rs = oracle_lib.reduce([c for c, _ in q], [s for _, s in q], block)
+    assert_same_codes(to_host(oc), rc, "chunked codes")
+    assert_same_f32(to_host(os_), rs, "chunked scales")
+    if out_kind is not None:
+        _same_out(to_host(out), oracle_lib.dequantize(rc, rs, block, out_kind), out_kind, "chunked out")
+    # the same cut through the pipelined call, which orders the streams itself
+    oc.fill_(0x55)
+    os_.fill_(-1.0)
+    qar.qar_reduce_quantized_pipelined(dc, ds, block, nchunks, streams, oc, os_)
+    torch.cuda.synchronize()
+    assert_same_codes(to_host(oc), rc, "pipelined codes")
+    assert_same_f32(to_host(os_), rs, "pipelined scales")
 
 
 @pytest.mark.parametrize("case", range(CASES // 4))
