@@ -588,7 +588,7 @@ def summarize_kernel_trace(d: str, out_dir: str = PROFILES) -> int:
     for (name, grid), d_us in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         m = re.match(r"qar::(\w+)<(\d+)?", name)
         kern, B = m.group(1), int(m.group(2)) if m.group(2) else None   # the comparator has no block
-        if "RowLanes" in name:
+        if "RowLanes" in name or kern.endswith("_rows"):
             what = "rows: N=8 x [8192, 2880] (row layout)"
             elems = "-"
         else:
@@ -615,8 +615,8 @@ python bench.py --summarize-kernel-trace gpurun_out/prof
 Durations from the trace (dispatch start to end), microseconds, over all dispatches of the run (preheat,
 warm-up, timed regions and the extras), one row per kernel and launch size. Grid x is threads: 16 elements
 per lane, 8 for the kernels whose name ends in 8 (`k_reduce8`, `k_quantize_reduce8`). Template arguments:
-`k_reduce<B, OUT, lane map, codes>`, `k_reduce8<B, OUT, codes>`, `k_quantize_reduce<B, OUT, input, codes,
-dense loads>`, with OUT 0 = bf16 output fused, 1 = fp32, -1 = none; codes `Int8Codes`, `E4M3Codes` or
+`k_reduce<B, OUT, lane map, codes>`, `k_reduce8<B, OUT, codes>`, `k_reduce8_rows<B, OUT>` (row-bounded blocks,
+8 elements per lane), `k_quantize_reduce<B, OUT, input, codes, dense loads>`, with OUT 0 = bf16 output fused, 1 = fp32, -1 = none; codes `Int8Codes`, `E4M3Codes` or
 `Int4Codes`. The headline kernel (one chunk of the chunked small-block reduce) is in bold; its timed steps
 alone are split out in `k_reduce_smallblock_chunked_trace.md`. Rows are in order of total GPU time.
 
@@ -1804,8 +1804,10 @@ def pipelined_bench(qar, torch, synth, dev, skew):
 
 def rows_bench(qar, torch, dev):
     """Row-bounded blocks on a [8192, 2880] bf16 tensor (2880 = 11 blocks of
-    256 + a partial block of 64 per row), N=8: quantize and the fused reduce
-    with bf16 out through the general one-wavefront-per-block kernels."""
+    256 + a partial block of 64 per row), N=8: quantize (16 elements per
+    lane) and the fused reduce with bf16 and with fp32 output (8 per lane),
+    through the row-bounded lane kernels (the row length is a multiple of
+    16)."""
     rows, row_len, B, N = 8192, 2880, 256, 8
     n = rows * row_len
     nb = qar.row_blocks(rows, row_len, B)
@@ -1830,6 +1832,9 @@ def rows_bench(qar, torch, dev):
     res = {"shape": f"N={N} x [{rows}, {row_len}] bf16, block {B} (partial last block of 64 per row)",
            "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 50)),
            "reduce_fused_bf16_out": _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fr, nsets, 50))}
+    sets = [(c, s, co, so, None, x) for c, s, co, so, _, x in sets]      # free the bf16 outputs first
+    sets = [(c, s, co, so, torch.empty(n, dtype=torch.float32, device=dev), x) for c, s, co, so, _, x in sets]
+    res["reduce_fused_f32_out"] = _rate((N + 1) * qbytes + 4 * n, _loop_us(torch, fr, nsets, 50))
     del sets, xs
     torch.cuda.empty_cache()
     return res

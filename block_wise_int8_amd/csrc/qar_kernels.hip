@@ -29,54 +29,83 @@ namespace qar {
 // ---------------------------------------------------------------------------
 // where each lane works
 //
-// Global lane g owns 16 consecutive elements starting at e0, inside block
-// blk; the B/16 lanes of a block are adjacent (one DPP row or part of one).
-//   FlatLanes: blocks tile the buffer: e0 = 16 g, blk = e0 / B.
-//   RowLanes:  row-bounded blocks of a [rows, row_len] tensor with
-//              row_len % 16 == 0: block blk = (row r, k-th block of the
-//              row) starts at r * row_len + k * B; lanes past the end of a
-//              row's partial last block are invalid and contribute nothing
-//              to the block's absmax.
+// Global lane g owns P consecutive elements starting at e0, inside block
+// blk; the B/P lanes of a block are adjacent (one DPP row, part of one, or
+// two).  P is 16 (FlatLanes, RowLanes) or 8 (FlatLanes8, RowLanes8: the
+// reduce's narrow kernels).
+//   Flat: blocks tile the buffer: e0 = P g, blk = e0 / B.
+//   Rows: row-bounded blocks of a [rows, row_len] tensor with
+//         row_len % 16 == 0: block blk = (row r, k-th block of the row)
+//         starts at r * row_len + k * B; lanes past the end of a row's
+//         partial last block are invalid and contribute nothing to the
+//         block's absmax.
 // Invalid lanes read element 0 (any finite value) and store nothing.
 struct LaneAt {
     size_t e0, blk;
     bool valid, leads; // leads: first lane of its block (writes the scale)
 };
 
+constexpr int kLaneElems8 = 8;
+
+template <int B, int P>
+__device__ __forceinline__ LaneAt flat_lane(size_t g, size_t n) {
+    LaneAt a;
+    a.e0 = g * P;
+    a.valid = a.e0 < n;
+    a.blk = a.e0 / B;
+    a.leads = a.e0 % B == 0;
+    return a;
+}
+
+template <int B, int P>
+__device__ __forceinline__ LaneAt row_lane(size_t g, size_t row_len, size_t nblocks, uint32_t per_row) {
+    constexpr uint32_t L = B / P;
+    LaneAt a;
+    a.blk = g / L;
+    const uint32_t j = (uint32_t)(g % L);
+    const uint32_t b32 = (uint32_t)a.blk; // nblocks < 2^26
+    const uint32_t r = b32 / per_row, k = b32 - r * per_row;
+    const size_t col = (size_t)k * B + (size_t)j * P;
+    a.e0 = (size_t)r * row_len + col;
+    a.valid = a.blk < nblocks && col < row_len;
+    a.leads = j == 0;
+    return a;
+}
+
 template <int B>
 struct FlatLanes {
     size_t n;
+    static constexpr int kLane = kLaneElems;
     static constexpr bool kContiguous = true; // a wave covers 1024 consecutive elements
     static constexpr bool kPartialBlocks = false;
-    __device__ __forceinline__ LaneAt at(size_t g) const {
-        LaneAt a;
-        a.e0 = g * kLaneElems;
-        a.valid = a.e0 < n;
-        a.blk = a.e0 / B;
-        a.leads = a.e0 % B == 0;
-        return a;
-    }
+    __device__ __forceinline__ LaneAt at(size_t g) const { return flat_lane<B, kLane>(g, n); }
 };
 
 template <int B>
 struct RowLanes {
     size_t row_len, nblocks;
     uint32_t per_row; // blocks per row
+    static constexpr int kLane = kLaneElems;
     static constexpr bool kContiguous = false;
     static constexpr bool kPartialBlocks = true;
-    __device__ __forceinline__ LaneAt at(size_t g) const {
-        constexpr uint32_t L = B / kLaneElems;
-        LaneAt a;
-        a.blk = g / L;
-        const uint32_t j = (uint32_t)(g % L);
-        const uint32_t b32 = (uint32_t)a.blk; // nblocks < 2^26
-        const uint32_t r = b32 / per_row, k = b32 - r * per_row;
-        const size_t col = (size_t)k * B + (size_t)j * kLaneElems;
-        a.e0 = (size_t)r * row_len + col;
-        a.valid = a.blk < nblocks && col < row_len;
-        a.leads = j == 0;
-        return a;
-    }
+    __device__ __forceinline__ LaneAt at(size_t g) const { return row_lane<B, kLane>(g, row_len, nblocks, per_row); }
+};
+
+template <int B>
+struct FlatLanes8 {
+    size_t n;
+    static constexpr int kLane = kLaneElems8;
+    static constexpr bool kPartialBlocks = false;
+    __device__ __forceinline__ LaneAt at(size_t g) const { return flat_lane<B, kLane>(g, n); }
+};
+
+template <int B>
+struct RowLanes8 {
+    size_t row_len, nblocks;
+    uint32_t per_row;
+    static constexpr int kLane = kLaneElems8;
+    static constexpr bool kPartialBlocks = true;
+    __device__ __forceinline__ LaneAt at(size_t g) const { return row_lane<B, kLane>(g, row_len, nblocks, per_row); }
 };
 
 // absmax over a lane's values, zero for an invalid lane of a partial block
@@ -448,13 +477,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restri
 // its last load.  A lane's 8 codes are 8 bytes (4 for 4-bit codes),
 // contiguous across the wavefront, and so are its 8 bf16 inputs and outputs
 // (16 bytes), so the output needs no staging.  A block of B elements is B/8
-// adjacent lanes (8 to 32) of one wavefront.  The launchers below say where
-// these kernels are used and what was measured.
-constexpr int kLaneElems8 = 8;
+// adjacent lanes (8 to 32) of one wavefront.  Lanes is FlatLanes8 or, for
+// the row-bounded reduce, RowLanes8.  The launchers below say where these
+// kernels are used and what was measured.
 constexpr int kTileElems8 = kThreads * kLaneElems8;
 
-template <int B, int OUT, typename OwnIn, typename C, bool kDense>
-__device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n, int8_t* codes_out,
+template <int B, int OUT, typename OwnIn, typename C, bool kDense, typename Lanes>
+__device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, Lanes lanes, int8_t* codes_out,
                                               float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                               const OwnIn* __restrict__ x_own, int own,
                                               int8_t* __restrict__ own_codes, float* __restrict__ own_scales,
@@ -467,10 +496,9 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
     using Pack = typename C::template Pack<P>;
     for (uint32_t t = map.first(blockIdx.x, gridDim.x); t < ntiles; t += gridDim.x) {
         const uint32_t tile = map.tile(t);
-        const size_t e0 = ((size_t)tile * kThreads + threadIdx.x) * P;
-        const bool valid = e0 < n; // n % B == 0: a block is wholly inside or outside
-        const size_t ld = valid ? e0 : 0;
-        const size_t blk = ld / B;
+        const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
+        const size_t ld = a.valid ? a.e0 : 0;
+        const size_t blk = a.valid ? a.blk : 0;
         uint4 xr[kRawWords];
         if constexpr (kOwn) {
 #pragma unroll
@@ -513,11 +541,12 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
                     float m = 0.0f;
 #pragma unroll
                     for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(v[i]));
+                    if constexpr (Lanes::kPartialBlocks) m = a.valid ? m : 0.0f;
                     s_own = lanes_max<L>(m) / C::kQmax;
                     q_own = C::template quantize_p<P>(v, s_own);
-                    if (valid) {
-                        C::template store_p<P>(own_codes, e0, q_own);
-                        if (e0 % B == 0) own_scales[e0 / B] = s_own;
+                    if (a.valid) {
+                        C::template store_p<P>(own_codes, a.e0, q_own);
+                        if (a.leads) own_scales[a.blk] = s_own;
                     }
                 }
 #pragma unroll
@@ -546,11 +575,13 @@ __device__ __forceinline__ void reduce_tiles8(RankPtrs rp, int nranks, size_t n,
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(acc[i]));
+        if constexpr (Lanes::kPartialBlocks) m = a.valid ? m : 0.0f;
         const float so = lanes_max<L>(m) / C::kQmax;
         const Pack qo = C::template quantize_p<P>(acc, so);
-        if (valid) {
+        if (a.valid) {
+            const size_t e0 = a.e0;
             C::template store_p<P>(codes_out, e0, qo);
-            if (e0 % B == 0) scales_out[e0 / B] = so;
+            if (a.leads) scales_out[a.blk] = so;
             if constexpr (OUT != kOutNone) {
                 float y[P];
                 C::template dequantize_p<P>(qo, so, y);
@@ -576,8 +607,17 @@ template <int B, int OUT, typename C>
 __global__ __launch_bounds__(kThreads) void k_reduce8(RankPtrs rp, int nranks, size_t n, int8_t* codes_out,
                                                       float* scales_out, void* __restrict__ out, uint32_t ntiles,
                                                       TileMap map) {
-    reduce_tiles8<B, OUT, void, C, false>(rp, nranks, n, codes_out, scales_out, out, ntiles, nullptr, -1, nullptr,
-                                          nullptr, map);
+    reduce_tiles8<B, OUT, void, C, false>(rp, nranks, FlatLanes8<B>{n}, codes_out, scales_out, out, ntiles,
+                                          nullptr, -1, nullptr, nullptr, map);
+}
+
+// the row-bounded reduce (int8 codes) with 8 elements per lane
+template <int B, int OUT>
+__global__ __launch_bounds__(kThreads) void k_reduce8_rows(RankPtrs rp, int nranks, RowLanes8<B> lanes,
+                                                           int8_t* codes_out, float* scales_out,
+                                                           void* __restrict__ out, uint32_t ntiles) {
+    reduce_tiles8<B, OUT, void, Int8Codes, false>(rp, nranks, lanes, codes_out, scales_out, out, ntiles, nullptr,
+                                                  -1, nullptr, nullptr, TileMap{0, 0, 1, 1});
 }
 
 template <int B, int OUT, typename In, typename C, bool kDense>
@@ -586,8 +626,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce8(const In* __restr
                                                                int nranks, size_t n, int8_t* codes_out,
                                                                float* scales_out, void* __restrict__ out,
                                                                uint32_t ntiles, uint32_t super) {
-    reduce_tiles8<B, OUT, In, C, kDense>(rp, nranks, n, codes_out, scales_out, out, ntiles, x_own, own, own_codes,
-                                         own_scales, TileMap{super, 0, 1, 1});
+    reduce_tiles8<B, OUT, In, C, kDense>(rp, nranks, FlatLanes8<B>{n}, codes_out, scales_out, out, ntiles, x_own,
+                                         own, own_codes, own_scales, TileMap{super, 0, 1, 1});
 }
 
 // ---------------------------------------------------------------------------
@@ -1027,6 +1067,28 @@ hipError_t quantize_b(const void* x, int in_kind, Lanes lanes, Grid g, int8_t* c
     });
 }
 
+// The reduce with 8 elements per lane (reduce_tiles8) for int8 and E4M3
+// codes from 6 to 8 ranks, and from 4 with a fused output; 16 per lane for
+// fewer ranks, for more, and for 4-bit codes.  Measured with B = 256, one
+// launch per call, µs (16 -> 8 per lane), no output / bf16 output:
+//   16.8M elements: N=1 9.7 -> 12.9 / 14.6 -> 17.3; N=3 14.0 -> 16.1 /
+//     19.6 -> 19.8; N=4 16.1 -> 17.4 / 22.0 -> 21.6; N=6 21.3 -> 21.1 /
+//     26.8 -> 26.1; N=8 26.7 -> 26.1 / 32.8 -> 31.6
+//   8.4M: N=4 9.95 -> 10.54 / 13.47 -> 12.84; N=6 12.72 -> 12.46 / 15.75 ->
+//     15.12; N=8 15.59 -> 15.12 / 18.33 -> 18.02
+//   4.2M: N=6 8.12 -> 8.65 / 9.58 -> 9.97; N=8 9.96 -> 9.87 / 11.39 -> 11.43
+//   2.1M: N=4 5.15 -> 4.83 / 5.24 -> 5.03; N=8 6.73 -> 6.08 / 6.90 -> 6.34
+// Few ranks leave too little arithmetic per element to pay for the lane's
+// fixed work twice as often.  With N = 16 (67M elements, B = 64) twice the
+// load instructions per byte cost more than they give: 8 chunks over 4
+// streams 202.9 -> 210.1.  4-bit codes (4 bytes per lane): 17.8 -> 21.0 at
+// 16.8M elements.
+constexpr int kMaxRanks8 = 8;
+
+bool reduce_is_narrow(int code, int nranks, int out_kind) {
+    return code != kCodeInt4 && nranks <= kMaxRanks8 && (nranks >= 6 || (out_kind != kOutNone && nranks >= 4));
+}
+
 template <int B, typename Lanes, typename C = Int8Codes>
 hipError_t reduce_b(const RankPtrs& rp, int nranks, Lanes lanes, Grid g, int8_t* codes_out, float* scales_out,
                     void* out, int out_kind, hipStream_t st) {
@@ -1057,28 +1119,57 @@ hipError_t dequantize_b(const int8_t* codes, const float* scales, size_t n, void
     return launch(k_dequantize<B, float, C>, g.blocks, st, codes, scales, n, static_cast<float*>(out), g.ntiles);
 }
 
-template <int B>
-RowLanes<B> row_lanes(const RowsCall& c, size_t& nlanes) {
-    RowLanes<B> l;
+// RowLanes<B> or RowLanes8<B> of a row-bounded call, and its lane count
+template <int B, typename RL>
+RL row_lanes(const RowsCall& c, size_t& nlanes) {
+    RL l;
     l.row_len = c.row_len;
     l.per_row = (uint32_t)((c.row_len + B - 1) / B);
     l.nblocks = c.rows * l.per_row;
-    nlanes = l.nblocks * (B / kLaneElems);
+    nlanes = l.nblocks * (B / RL::kLane);
     return l;
 }
 
-// row-bounded blocks, row_len % 16 == 0: the vector kernels on RowLanes
+// row-bounded blocks, row_len % 16 == 0: the vector kernels on RowLanes.
+// The reduce with a fused output takes 8 elements per lane (fp32 output: any
+// rank count; bf16: from 3 ranks), where a lane's 8 results are one or two
+// 16-byte stores that the wavefront's lanes write contiguously, instead of
+// 16 per lane, whose two or four stores per lane each cover a part of every
+// line.  Measured on [8192, 2880] bf16 data, B = 256 (the last block of a
+// row 64 elements), µs, 16 -> 8 per lane, bit-identical:
+//   fp32 out: N=1 83.7 -> 34.3; N=4 83.5 -> 44.5; N=8 91.0 -> 61.3;
+//     N=16 128.2 -> 96.0
+//   bf16 out: N=1 22.1 -> 25.4; N=2 25.7 -> 26.4; N=3 29.4 -> 28.5;
+//     N=8 48.4 -> 47.0; N=16 84.4 -> 83.5 (B = 64, [8192, 2912], N=8:
+//     49.8 -> 47.9)
+//   no output: N=1 15.9 -> 20.7; N=8 38.9 -> 40.1; N=16 73.4 -> 77.2, so
+//     it keeps 16 per lane.
+bool rows_reduce_is_narrow(int nranks, int out_kind) {
+    return out_kind == kOutF32 || (out_kind == kOutBF16 && nranks >= 3);
+}
+
 template <int B>
 hipError_t rows_vector(const RowsCall& c, hipStream_t st) {
     size_t nlanes = 0;
-    const RowLanes<B> l = row_lanes<B>(c, nlanes);
+    const RowLanes<B> l = row_lanes<B, RowLanes<B>>(c, nlanes);
     const Grid g = grid_lanes(nlanes);
     switch (c.op) {
     case kRowsQuantize:
         return quantize_b<B>(c.x, c.kind, l, g, c.codes_out, c.scales_out, st);
-    case kRowsReduce:
-        return reduce_b<B>(c.rp, c.nranks, l, g, c.codes_out, c.scales_out, c.out,
-                           c.out ? (c.kind == kInBF16 ? kOutBF16 : kOutF32) : kOutNone, st);
+    case kRowsReduce: {
+        const int out_kind = c.out ? (c.kind == kInBF16 ? kOutBF16 : kOutF32) : kOutNone;
+        if (rows_reduce_is_narrow(c.nranks, out_kind)) {
+            size_t nlanes8 = 0;
+            const RowLanes8<B> l8 = row_lanes<B, RowLanes8<B>>(c, nlanes8);
+            const Grid g8 = grid_lanes(nlanes8); // 256 lanes per tile at either width
+            return dispatch_out(out_kind, [&](auto oc) {
+                constexpr int OUT = decltype(oc)::value;
+                return launch(k_reduce8_rows<B, OUT>, g8.blocks, st, c.rp, c.nranks, l8, c.codes_out, c.scales_out,
+                              c.out, g8.ntiles);
+            });
+        }
+        return reduce_b<B>(c.rp, c.nranks, l, g, c.codes_out, c.scales_out, c.out, out_kind, st);
+    }
     case kRowsRingStep:
         return ring_b<B>(c.codes_in, c.scales_in, c.x, c.kind, l, g, c.codes_out, c.scales_out, st);
     default:
@@ -1185,23 +1276,6 @@ hipError_t launch_quantize(const void* x, int in_kind, size_t n, int block, int8
     });
 }
 
-// The reduce with 8 elements per lane (reduce_tiles8) for int8 and E4M3
-// codes from 6 to 8 ranks, and from 4 with a fused output; 16 per lane for
-// fewer ranks, for more, and for 4-bit codes.  Measured with B = 256, one
-// launch per call, µs (16 -> 8 per lane), no output / bf16 output:
-//   16.8M elements: N=1 9.7 -> 12.9 / 14.6 -> 17.3; N=3 14.0 -> 16.1 /
-//     19.6 -> 19.8; N=4 16.1 -> 17.4 / 22.0 -> 21.6; N=6 21.3 -> 21.1 /
-//     26.8 -> 26.1; N=8 26.7 -> 26.1 / 32.8 -> 31.6
-//   8.4M: N=4 9.95 -> 10.54 / 13.47 -> 12.84; N=6 12.72 -> 12.46 / 15.75 ->
-//     15.12; N=8 15.59 -> 15.12 / 18.33 -> 18.02
-//   4.2M: N=6 8.12 -> 8.65 / 9.58 -> 9.97; N=8 9.96 -> 9.87 / 11.39 -> 11.43
-//   2.1M: N=4 5.15 -> 4.83 / 5.24 -> 5.03; N=8 6.73 -> 6.08 / 6.90 -> 6.34
-// Few ranks leave too little arithmetic per element to pay for the lane's
-// fixed work twice as often.  With N = 16 (67M elements, B = 64) twice the
-// load instructions per byte cost more than they give: 8 chunks over 4
-// streams 202.9 -> 210.1.  4-bit codes (4 bytes per lane): 17.8 -> 21.0 at
-// 16.8M elements.
-constexpr int kMaxRanks8 = 8;
 
 // Super-tiles of 64 tiles dealt round-robin to the XCDs instead of one range
 // per XCD, for reduces of at least 8 ranks over at least 2^25 elements.
@@ -1251,8 +1325,7 @@ hipError_t launch_reduce(const RankPtrs& rp, int nranks, size_t n, int block, in
             constexpr int B = decltype(bc)::value;
             return dispatch_out(out_kind, [&](auto oc) {
                 constexpr int OUT = decltype(oc)::value;
-                if (!std::is_same<C, Int4Codes>::value && nranks <= kMaxRanks8 &&
-                    (nranks >= 6 || (OUT != kOutNone && nranks >= 4))) {
+                if (reduce_is_narrow(code, nranks, OUT)) {
                     const ReduceGrid g = reduce_grid(nranks, n, kTileElems8, chunk);
                     if (g.blocks == 0) return hipSuccess;
                     return launch(k_reduce8<B, OUT, C>, g.blocks, st, rp, nranks, n, codes_out, scales_out, out,

@@ -68,7 +68,7 @@ def test_quantize_and_dequantize_rows(oracle_lib, rows, row_len, block, kind):
 
 
 @pytest.mark.parametrize("out", [None, "bf16", "f32"])
-@pytest.mark.parametrize("nranks", [1, 3, 8])
+@pytest.mark.parametrize("nranks", [1, 2, 3, 8, 12])
 @pytest.mark.parametrize("rows,row_len,block", SHAPES[:4])
 def test_reduce_rows(oracle_lib, rows, row_len, block, nranks, out):
     xs = [_data(100 * r + row_len, rows, row_len, "bf16", outlier=9.0e36) for r in range(nranks)]
@@ -93,6 +93,35 @@ def test_reduce_rows(oracle_lib, rows, row_len, block, nranks, out):
             assert_same_bits16(to_host(o), want, "fused out")
         else:
             assert_same_f32(to_host(o), want, "fused out")
+
+
+def test_rows_reduce_at_bench_shape(oracle_lib):
+    """The row-bounded reduce at the shape bench.py times, N = 8 x [8192,
+    2880] bf16, B = 256 (every row ends in a partial block of 64): no output
+    (16 elements per lane), bf16 and fp32 output (8 per lane), each against
+    the oracle row by row."""
+    rows, row_len, B, N = 8192, 2880, 256, 8
+    xs = [_data(500 + r, rows, row_len, "bf16", outlier=9.0e36) for r in range(N)]
+    per_rank = [_split(*_oracle_quantize_rows(oracle_lib, x, B), rows, row_len, B) for x in xs]
+    del xs
+    dc = [to_dev(p[0].reshape(-1)) for p in per_rank]
+    ds = [to_dev(p[1].reshape(-1)) for p in per_rank]
+    red = [oracle_lib.reduce([p[0][r] for p in per_rank], [p[1][r] for p in per_rank], B) for r in range(rows)]
+    wc, ws = np.concatenate([c for c, _ in red]), np.concatenate([s for _, s in red])
+    for out in (None, "bf16", "f32"):
+        say(f"rows reduce at the bench shape N={N} {rows}x{row_len} B={B} out={out}")
+        o = None if out is None else torch.empty(rows * row_len, device="cuda:0",
+                                                 dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+        oc, os_ = qar.qar_reduce_quantized_rows(dc, ds, rows, row_len, B, out=o)
+        torch.cuda.synchronize()
+        assert_same_codes(to_host(oc), wc, f"codes (out={out})")
+        assert_same_f32(to_host(os_), ws, f"scales (out={out})")
+        if out is not None:
+            want = np.concatenate([oracle_lib.dequantize(c, s, B, out) for c, s in red])
+            if out == "bf16":
+                assert_same_bits16(to_host(o), want, "fused out")
+            else:
+                assert_same_f32(to_host(o), want, "fused out")
 
 
 @pytest.mark.parametrize("in_place", [False, True])
