@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 DOMINANT = "k_quantize_reduce8"  # the one-kernel step's kernel from 2^23 elements per rank on
+ROWS_SHAPE = (8192, 2880, 8)  # the row-bounded workload: rows, row length, ranks (11 blocks of 256 + one of 64 per row)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_wise_int8_amd", "csrc", f)
                   for f in ("qar_kernels.hip", "qar_device.h")]
@@ -235,6 +236,15 @@ def counter_catalogue():
     out.append(("ring_quantize", "ring quantize of rank 0 ([2048, 3840] bf16)",
                 "k_quantize<256, unsigned short, qar::FlatLanes<256>, qar::Int8Codes>", grid(w4.n), 2 * w4.n,
                 qb(w4.n, 256)))
+    rows, row_len, NR = ROWS_SHAPE
+    nr, nbr = rows * row_len, rows * -(-row_len // 256)
+    qr = nr + 4 * nbr
+    out.append(("rows_quantize", f"row-bounded quantize (one rank: [{rows}, {row_len}] bf16, B=256)",
+                "k_quantize<256, unsigned short, qar::RowLanes<256>, qar::Int8Codes>", nbr * 16, 2 * nr, qr))
+    out.append(("rows_reduce_bf16", f"row-bounded fused reduce + bf16 out (N={NR})",
+                "k_reduce8_rows<256, 0>", nbr * 32, NR * qr, qr + 2 * nr))
+    out.append(("rows_reduce_f32", f"row-bounded fused reduce + fp32 out (N={NR})",
+                "k_reduce8_rows<256, 1>", nbr * 32, NR * qr, qr + 4 * nr))
     return out
 
 
@@ -363,6 +373,35 @@ def counter_run(qar, torch, synth, dev) -> int:
     for x, c, s_, loc, co, so in ss[reps:]:
         qar.qar_quantize_blocks(x, B, c, s_)
     torch.cuda.synchronize()
+    del ss, x0, x1
+    torch.cuda.empty_cache()
+
+    # row-bounded blocks: quantize, the fused reduce with bf16 and with fp32 out
+    rows, row_len, N = ROWS_SHAPE
+    B, n = 256, rows * row_len
+    nb = qar.row_blocks(rows, row_len, B)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    q = [qar.qar_quantize_rows(torch.randn(rows, row_len, generator=g, device=dev).to(torch.bfloat16), B)
+         for _ in range(N)]
+    ss = sets_of(lambda: ([c.clone() for c, _ in q], [s_.clone() for _, s_ in q],
+                          torch.empty(n, dtype=torch.int8, device=dev), torch.empty(nb, dtype=torch.float32, device=dev),
+                          torch.randn(rows, row_len, generator=g, device=dev).to(torch.bfloat16)), reps)
+    del q
+    torch.cuda.synchronize()
+    say("rows_quantize")
+    for c, s_, co, so, x in ss:
+        qar.qar_quantize_rows(x, B, co, so)
+    torch.cuda.synchronize()
+    for kind, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        say(f"rows_reduce_{kind}")
+        outs = [torch.empty(n, dtype=dt, device=dev) for _ in range(2)]
+        for i, (c, s_, co, so, x) in enumerate(ss):
+            qar.qar_reduce_quantized_rows(c, s_, rows, row_len, B, co, so, out=outs[i % 2])
+        torch.cuda.synchronize()
+        del outs
+    del ss
+    torch.cuda.empty_cache()
     print(json.dumps({"counter_run": "done", "catalogue": [e[0] for e in counter_catalogue()]}), flush=True)
     return 0
 
@@ -534,6 +573,9 @@ _BENCH_TIMES = {
     "prefill_reduce_bf16": (("prefill", "avg_us"),),
     "ring_step": (("ring_step", "graph_replay", "avg_us"),),
     "ring_quantize": (("ring_step", "quantize", "avg_us"),),
+    "rows_quantize": (("row_bounded", "quantize", "avg_us"),),
+    "rows_reduce_bf16": (("row_bounded", "reduce_fused_bf16_out", "avg_us"),),
+    "rows_reduce_f32": (("row_bounded", "reduce_fused_f32_out", "avg_us"),),
 }
 
 
@@ -1808,7 +1850,7 @@ def rows_bench(qar, torch, dev):
     lane) and the fused reduce with bf16 and with fp32 output (8 per lane),
     through the row-bounded lane kernels (the row length is a multiple of
     16)."""
-    rows, row_len, B, N = 8192, 2880, 256, 8
+    (rows, row_len, N), B = ROWS_SHAPE, 256
     n = rows * row_len
     nb = qar.row_blocks(rows, row_len, B)
     g = torch.Generator(device=dev)
