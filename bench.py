@@ -208,6 +208,8 @@ def counter_catalogue():
                 "k_reduce8<256, -1, qar::Int8Codes>", grid8(n2), N2 * qb(n2, 256), qb(n2, 256)))
     out.append(("outliers_reduce_bf16", f"outlier fused reduce + bf16 out (N={N2})",
                 "k_reduce8<256, 0, qar::Int8Codes>", grid8(n2), N2 * qb(n2, 256), qb(n2, 256) + 2 * n2))
+    out.append(("outliers_reduce_f32", f"outlier fused reduce + fp32 out (N={N2})",
+                "k_reduce8<256, 1, qar::Int8Codes>", grid8(n2), N2 * qb(n2, 256), qb(n2, 256) + 4 * n2))
     out.append(("outliers_dequantize", "outlier dequantize to bf16",
                 "k_dequantize<256, unsigned short, qar::Int8Codes>", grid(n2), qb(n2, 256), 2 * n2))
     out.append(("outliers_comparator", f"unquantized bf16 comparator (N={N2})",
@@ -313,6 +315,12 @@ def counter_run(qar, torch, synth, dev) -> int:
             for c, s_, co, so, out, x in ss:
                 red(c, s_, B, co, so, out=out)
             torch.cuda.synchronize()
+            say("outliers_reduce_f32")
+            outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
+            for i, (c, s_, co, so, out, x) in enumerate(ss):
+                red(c, s_, B, co, so, out=outs[i % 2])
+            torch.cuda.synchronize()
+            del outs
             say("outliers_quantize")
             for c, s_, co, so, out, x in ss:
                 quant(x, B, c[0], s_[0])
@@ -563,6 +571,7 @@ _BENCH_TIMES = {
     "outliers_quantize": (("outliers_step", "kernels", "k_quantize", "graph_replay", "avg_us"),),
     "outliers_reduce": (("reduce_only", "avg_us"),),
     "outliers_reduce_bf16": (("outliers_step", "kernels", "k_reduce (bf16 out)", "avg_us"),),
+    "outliers_reduce_f32": (("reduce_only", "f32_out", "avg_us"),),
     "outliers_dequantize": (("dequantize", "graph_replay", "avg_us"),),
     "outliers_comparator": (("unquantized_comparator", "avg_us"),),
     "outliers_reduce_e4m3": (("code_formats", "timing_outliers", "e4m3", "reduce_no_out", "avg_us"),),
@@ -1437,11 +1446,21 @@ def reduce_only(args, qar, torch, sets, B, N, n, qbytes):
         qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"], stream=stream)
     us, us_min = _loop_us(torch, fn, len(sets), reps, warmup=5, with_min=True)
     nbytes = (N + 1) * qbytes
-    return {"avg_us": round(us, 3), "min_us": round(us_min, 3), "algorithmic_bytes": nbytes,
-            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "payload_GBps": round(N * n * 2 / (us * 1e-6) / 1e9, 1),
-            "note": "back-to-back launches over rotated buffer sets, out=NULL"}
+    res = {"avg_us": round(us, 3), "min_us": round(us_min, 3), "algorithmic_bytes": nbytes,
+           "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "payload_GBps": round(N * n * 2 / (us * 1e-6) / 1e9, 1),
+           "note": "back-to-back launches over rotated buffer sets, out=NULL"}
+    outs = [torch.empty(n, dtype=torch.float32, device=sets[0]["codes_out"].device) for _ in sets]
+
+    def ff(i):
+        st = sets[i % len(sets)]
+        qar.qar_reduce_quantized(st["codes"], st["scales"], B, st["codes_out"], st["scales_out"],
+                                 out=outs[i % len(sets)], stream=stream)
+    us, us_min = _loop_us(torch, ff, len(sets), reps, warmup=5, with_min=True)
+    res["f32_out"] = _rate(nbytes + 4 * n, (us, us_min))
+    del outs
+    return res
 
 
 # Back-to-back launches of a kernel that does arithmetic besides streaming
