@@ -478,10 +478,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_reduce(const In* __restri
 // the wavefronts, each with half the registers and half the arithmetic after
 // its last load.  A lane's 8 codes are 8 bytes (4 for 4-bit codes),
 // contiguous across the wavefront, and so are its 8 bf16 inputs and outputs
-// (16 bytes), so the output needs no staging.  A block of B elements is B/8
-// adjacent lanes (8 to 32) of one wavefront.  Lanes is FlatLanes8 or, for
-// the row-bounded reduce, RowLanes8.  The launchers below say where these
-// kernels are used and what was measured.
+// (16 bytes), so a bf16 output needs no staging (an fp32 output goes
+// through store_f32_tile8).  A block of B elements is B/8 adjacent lanes (8
+// to 32) of one wavefront.  Lanes is FlatLanes8 or, for the row-bounded
+// reduce, RowLanes8.  The launchers below say where these kernels are used
+// and what was measured.
 constexpr int kTileElems8 = kThreads * kLaneElems8;
 
 // The fp32 output of a wave's 512 elements with 8 elements per lane: a
