@@ -243,6 +243,10 @@ def counter_catalogue():
     qr = nr + 4 * nbr
     out.append(("rows_quantize", f"row-bounded quantize (one rank: [{rows}, {row_len}] bf16, B=256)",
                 "k_quantize<256, unsigned short, qar::RowLanes<256>, qar::Int8Codes>", nbr * 16, 2 * nr, qr))
+    out.append(("rows_dequantize_bf16", f"row-bounded dequantize to bf16 ([{rows}, {row_len}])",
+                "k_dequantize_lanes<256, unsigned short>", nbr * 32, qr, 2 * nr))
+    out.append(("rows_dequantize_f32", f"row-bounded dequantize to fp32 ([{rows}, {row_len}])",
+                "k_dequantize_lanes<256, float>", nbr * 64, qr, 4 * nr))
     out.append(("rows_reduce_bf16", f"row-bounded fused reduce + bf16 out (N={NR})",
                 "k_reduce8_rows<256, 0>", nbr * 32, NR * qr, qr + 2 * nr))
     out.append(("rows_reduce_f32", f"row-bounded fused reduce + fp32 out (N={NR})",
@@ -402,8 +406,12 @@ def counter_run(qar, torch, synth, dev) -> int:
         qar.qar_quantize_rows(x, B, co, so)
     torch.cuda.synchronize()
     for kind, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
-        say(f"rows_reduce_{kind}")
         outs = [torch.empty(n, dtype=dt, device=dev) for _ in range(2)]
+        say(f"rows_dequantize_{kind}")
+        for i, (c, s_, co, so, x) in enumerate(ss):
+            qar.qar_dequantize_rows(c[1], s_[1], rows, row_len, B, out=outs[i % 2])
+        torch.cuda.synchronize()
+        say(f"rows_reduce_{kind}")
         for i, (c, s_, co, so, x) in enumerate(ss):
             qar.qar_reduce_quantized_rows(c, s_, rows, row_len, B, co, so, out=outs[i % 2])
         torch.cuda.synchronize()
@@ -583,6 +591,8 @@ _BENCH_TIMES = {
     "ring_step": (("ring_step", "graph_replay", "avg_us"),),
     "ring_quantize": (("ring_step", "quantize", "avg_us"),),
     "rows_quantize": (("row_bounded", "quantize", "avg_us"),),
+    "rows_dequantize_bf16": (("row_bounded", "dequantize_bf16", "avg_us"),),
+    "rows_dequantize_f32": (("row_bounded", "dequantize_f32", "avg_us"),),
     "rows_reduce_bf16": (("row_bounded", "reduce_fused_bf16_out", "avg_us"),),
     "rows_reduce_f32": (("row_bounded", "reduce_fused_f32_out", "avg_us"),),
 }
@@ -639,7 +649,7 @@ def summarize_kernel_trace(d: str, out_dir: str = PROFILES) -> int:
     for (name, grid), d_us in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         m = re.match(r"qar::(\w+)<(\d+)?", name)
         kern, B = m.group(1), int(m.group(2)) if m.group(2) else None   # the comparator has no block
-        if "RowLanes" in name or kern.endswith("_rows"):
+        if "RowLanes" in name or kern.endswith("_rows") or kern == "k_dequantize_lanes":
             what = "rows: N=8 x [8192, 2880] (row layout)"
             elems = "-"
         else:
@@ -1866,9 +1876,9 @@ def pipelined_bench(qar, torch, synth, dev, skew):
 def rows_bench(qar, torch, dev):
     """Row-bounded blocks on a [8192, 2880] bf16 tensor (2880 = 11 blocks of
     256 + a partial block of 64 per row), N=8: quantize (16 elements per
-    lane) and the fused reduce with bf16 and with fp32 output (8 per lane),
-    through the row-bounded lane kernels (the row length is a multiple of
-    16)."""
+    lane), dequantize to bf16 and fp32 (one 16-byte slot per lane) and the
+    fused reduce with bf16 and with fp32 output (8 per lane), through the
+    row-bounded lane kernels (the row length is a multiple of 16)."""
     (rows, row_len, N), B = ROWS_SHAPE, 256
     n = rows * row_len
     nb = qar.row_blocks(rows, row_len, B)
@@ -1890,12 +1900,17 @@ def rows_bench(qar, torch, dev):
         c, s, co, so, out, x = sets[i]
         qar.qar_reduce_quantized_rows(c, s, rows, row_len, B, co, so, out=out)
     qbytes = n + 4 * nb
+    def fd(i):
+        c, s, co, so, out, x = sets[i]
+        qar.qar_dequantize_rows(c[1], s[1], rows, row_len, B, out=out)
     res = {"shape": f"N={N} x [{rows}, {row_len}] bf16, block {B} (partial last block of 64 per row)",
            "quantize": _rate(2 * n + qbytes, _loop_us(torch, fq, nsets, 50)),
+           "dequantize_bf16": _rate(qbytes + 2 * n, _loop_us(torch, fd, nsets, 50)),
            "reduce_fused_bf16_out": _rate((N + 1) * qbytes + 2 * n, _loop_us(torch, fr, nsets, 50))}
     sets = [(c, s, co, so, None, x) for c, s, co, so, _, x in sets]      # free the bf16 outputs first
     sets = [(c, s, co, so, torch.empty(n, dtype=torch.float32, device=dev), x) for c, s, co, so, _, x in sets]
     res["reduce_fused_f32_out"] = _rate((N + 1) * qbytes + 4 * n, _loop_us(torch, fr, nsets, 50))
+    res["dequantize_f32"] = _rate(qbytes + 4 * n, _loop_us(torch, fd, nsets, 50))
     del sets, xs
     torch.cuda.empty_cache()
     return res

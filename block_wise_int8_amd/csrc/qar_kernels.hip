@@ -769,19 +769,51 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const int8_t* __restric
     }
 }
 
-// Row-bounded blocks with row_len % 16 == 0: each lane dequantizes its own
-// 16 codes.
+// Row-bounded blocks with row_len % 16 == 0: each lane dequantizes the
+// codes of one 16-byte output slot (8 bf16 or 4 fp32 elements), so that the
+// lanes of a block store one contiguous range per instruction.  Against
+// each lane storing its 16 elements directly (two or four 16-byte stores
+// that each cover part of every line), on [8192, 2880], B = 256, µs: bf16
+// 15.6 -> 14.2, fp32 81.0 -> 24.9 (B = 64, [8192, 2912], bf16: 16.5 ->
+// 14.2), bit-identical.  Two slots per lane, 64 slots apart: bf16 15.5,
+// fp32 26.0.
+template <int B, int P>
+struct RowSlots {
+    size_t row_len, nblocks;
+    uint32_t per_row;
+    static constexpr int kLane = P;
+    __device__ __forceinline__ LaneAt at(size_t g) const { return row_lane<B, P>(g, row_len, nblocks, per_row); }
+};
+
 template <int B, typename Out>
 __global__ __launch_bounds__(kThreads) void k_dequantize_lanes(const int8_t* __restrict__ codes,
                                                                const float* __restrict__ scales,
-                                                               RowLanes<B> lanes, Out* __restrict__ out,
-                                                               uint32_t ntiles) {
+                                                               RowSlots<B, 16 / sizeof(Out)> lanes,
+                                                               Out* __restrict__ out, uint32_t ntiles) {
+    constexpr int P = 16 / sizeof(Out);
     for (uint32_t tile = xcd_tile(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
         const LaneAt a = lanes.at((size_t)tile * kThreads + threadIdx.x);
         if (!a.valid) continue;
-        float y[kLaneElems];
-        dequantize16(load_b128(codes + a.e0), scales[a.blk], y);
-        store16(out + a.e0, y);
+        const float s = scales[a.blk];
+        uint4 o;
+        if constexpr (P == 8) {
+            const uint2 w = load_b64(codes + a.e0);
+            float y[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[k] = code_f32(w.x, k) * s;
+                y[4 + k] = code_f32(w.y, k) * s;
+            }
+            o = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                           pack_bf16x2(y[6], y[7]));
+        } else {
+            const uint32_t w = load_b32(codes + a.e0);
+            o = make_uint4(__builtin_bit_cast(uint32_t, code_f32(w, 0) * s),
+                           __builtin_bit_cast(uint32_t, code_f32(w, 1) * s),
+                           __builtin_bit_cast(uint32_t, code_f32(w, 2) * s),
+                           __builtin_bit_cast(uint32_t, code_f32(w, 3) * s));
+        }
+        store_b128(out + a.e0, o);
     }
 }
 
@@ -1240,8 +1272,12 @@ hipError_t rows_vector(const RowsCall& c, hipStream_t st) {
     default:
         return dispatch_in(c.kind, [&](auto ot) {
             using Out = typename decltype(ot)::type;
-            return launch(k_dequantize_lanes<B, Out>, g.blocks, st, c.codes_in, c.scales_in, l,
-                          static_cast<Out*>(c.out), g.ntiles);
+            using RS = RowSlots<B, 16 / sizeof(Out)>;
+            size_t nslots = 0;
+            const RS ls = row_lanes<B, RS>(c, nslots);
+            const Grid gs = grid_lanes(nslots); // 256 lanes per tile
+            return launch(k_dequantize_lanes<B, Out>, gs.blocks, st, c.codes_in, c.scales_in, ls,
+                          static_cast<Out*>(c.out), gs.ntiles);
         });
     }
 }
