@@ -1316,6 +1316,8 @@ def chunk_sweep(qar, torch, sets, B, N, n, qbytes, main_st, sides):
     for nchunks, strs, tag in ((8, [main_st] + sides, "caller + 3 side streams"),
                                (4, [main_st] + sides, "caller + 3 side streams"),
                                (16, [main_st] + sides, "caller + 3 side streams"),
+                               (32, [main_st] + sides, "caller + 3 side streams"),
+                               (64, [main_st] + sides, "caller + 3 side streams"),
                                (4, sides[:2], "2 side streams"),
                                (2, sides[:2], "2 side streams")):
         def fn(i, nchunks=nchunks, strs=strs):

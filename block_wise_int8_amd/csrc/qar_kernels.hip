@@ -1293,7 +1293,7 @@ uint32_t row_grid(size_t nblocks) { return (uint32_t)((nblocks + kThreads / 64 -
 // kept until the process ends.  In host code `scratch` names a host-side
 // stand-in, not device memory: its device address is looked up once per
 // device (that device current) and only that address is handed to kernels.
-__device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
 
 namespace {
 constexpr int kScratchDevices = 64;
