@@ -70,7 +70,19 @@
 extern "C" {
 #endif
 
-typedef enum qar_status {
+/* The enums below are passed by value across the ABI.  A C caller may pass
+ * any int in their place; compiled as C++ (the library itself) they take int
+ * as their fixed underlying type, so every such value is a value of the type
+ * and an unknown one reaches the argument checks (QAR_ERR_UNSUPPORTED or
+ * QAR_ERR_INVALID_ARG) instead of being undefined before them.  In C an
+ * enum is an int-sized integer type either way. */
+#ifdef __cplusplus
+#define QAR_ENUM_BASE : int
+#else
+#define QAR_ENUM_BASE
+#endif
+
+typedef enum qar_status QAR_ENUM_BASE {
     QAR_OK = 0,
     QAR_ERR_INVALID_ARG = 1, /* null pointer, n % block != 0, bad rank count, overlap */
     QAR_ERR_MISALIGNED = 2,  /* a pointer breaks the alignment rule above */
@@ -79,7 +91,7 @@ typedef enum qar_status {
     QAR_ERR_CAPACITY = 5     /* the call needs more static workspace than QAR_STATIC_WORKSPACE_BYTES */
 } qar_status;
 
-typedef enum qar_dtype {
+typedef enum qar_dtype QAR_ENUM_BASE {
     QAR_BF16 = 0, /* bfloat16, stored as 16-bit patterns */
     QAR_F32 = 1   /* IEEE binary32 */
 } qar_dtype;
@@ -267,7 +279,7 @@ qar_status qar_reduce_unquantized(const void* const* x, uint32_t nranks, size_t 
  * Results are bit-identical for every nchunks and nstreams under ONE_SHOT;
  * under RING they depend on nchunks through each chunk's starting rank.
  */
-typedef enum qar_schedule { QAR_SCHEDULE_ONE_SHOT = 0, QAR_SCHEDULE_RING = 1 } qar_schedule;
+typedef enum qar_schedule QAR_ENUM_BASE { QAR_SCHEDULE_ONE_SHOT = 0, QAR_SCHEDULE_RING = 1 } qar_schedule;
 
 qar_status qar_allreduce_simulated(const void* const* x, qar_dtype dtype, uint32_t nranks, size_t n,
                                    uint32_t block, qar_schedule schedule, int8_t* const* codes_work,
