@@ -1085,8 +1085,8 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
     overlaps the next one's ramp on other streams.
 
     Inputs: the recipe drawn on the GPU (synth.device_rank: torch's
-    generator), copied to the host for the CPU oracle, which quantizes and
-    reduces them on its own."""
+    generator), copied to the host for the CPU oracle once the GPU figures
+    are taken; the oracle quantizes and reduces them on its own."""
     w = synth.WORKLOADS["smallblock"]
     N, n, B = w.nranks, w.n, w.block
     nb = n // B
@@ -1103,21 +1103,13 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
             codes.append(c), scales.append(s_)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    host_x = [x.cpu().numpy() for x in xs] if not args.no_cpu_baseline else None
-    input_sha = [synth.sha256(h)[:16] for h in host_x] if host_x is not None else None
-    quant = None
-    if not args.no_extras:
-        # the quantize of one rank's fp32 buffer (A2-A4 on this workload), over the 16 inputs in turn
-        qc = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(2)]
-        qs = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(2)]
-
-        def fq(i):
-            qar.qar_quantize_blocks(xs[i % N], B, qc[i % 2], qs[i % 2], stream=main_st)
-        with torch.cuda.stream(main_st):
-            quant = _rate(4 * n + qbytes, _loop_us(torch, fq, N, 48, with_min=True))
-        quant["what"] = f"qar_quantize_blocks of one rank ({n:,} fp32, block {B}), the 16 ranks in turn"
-        del qc, qs
-    del xs
+    # The buffer sets are allocated right behind the inputs, before anything
+    # else allocates or copies: the inputs' copy to the host for the CPU
+    # oracle (4.3 GB) waits until the GPU figures are taken.  Allocated after
+    # that copy, the sets lay about 4.7 GB lower in the address space and the
+    # chunked step ran 3.5% slower on them (196.5-199.6 against 188.9-193.9
+    # us per step, one process each on one GPU; the single launch 188 us in
+    # both).
     nsets = 2                                   # 2 x 1.21 GB
     sets = []
     with torch.cuda.stream(main_st):
@@ -1199,7 +1191,7 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
             "workload": f"{w.key}: {w.description}",
             "nranks": N, "elements_per_rank": n, "block": B, "input_dtype": w.dtype,
             "seed": w.seed, "input_recipe": "synth.device_rank (torch's generator on the GPU, seeded)",
-            "input_sha256_16": input_sha,
+            "input_sha256_16": None,              # filled in with the host copies, after timing
             "step": (f"one-shot fused reduce (dequantize {N} quantized contributions, fp32 sum in rank order, "
                      f"requantize; no dequantized output) as one qar_reduce_quantized_chunked call: {CHUNKS} "
                      f"chunks over {STREAMS} streams (the caller's + {STREAMS - 1}), two chunks per stream; "
@@ -1233,16 +1225,28 @@ def smallblock_headline(args, qar, torch, np, synth, dev):
     }
     if not args.no_extras:
         result["chunk_sweep"] = chunk_sweep(qar, torch, sets, B, N, n, qbytes, main_st, sides)
+        # the quantize of one rank's fp32 buffer (A2-A4 on this workload), over the 16 inputs in turn
+        qc = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(2)]
+        qs = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(2)]
+
+        def fq(i):
+            qar.qar_quantize_blocks(xs[i % N], B, qc[i % 2], qs[i % 2], stream=main_st)
+        with torch.cuda.stream(main_st):
+            quant = _rate(4 * n + qbytes, _loop_us(torch, fq, N, 48, with_min=True))
+        quant["what"] = f"qar_quantize_blocks of one rank ({n:,} fp32, block {B}), the 16 ranks in turn"
+        del qc, qs
         result["smallblock_quantize"] = quant
-    if host_x is not None:
+    # the GPU figures are taken: now the host copies for the CPU oracle
+    host_x = gpu_c = gpu_s = None
+    if not args.no_cpu_baseline:
         gpu_c, gpu_s = sets[0]["co"].cpu().numpy(), sets[0]["so"].cpu().numpy()
-        del sets
-        torch.cuda.empty_cache()
+        host_x = [x.cpu().numpy() for x in xs]
+        result["config"]["input_sha256_16"] = [synth.sha256(h)[:16] for h in host_x]
+    del sets, xs
+    torch.cuda.empty_cache()
+    if host_x is not None:
         result["cpu_baseline"] = cpu_baseline_reduce(args, np, w, host_x, gpu_c, gpu_s)
         del host_x
-    else:
-        del sets
-    torch.cuda.empty_cache()
     if not args.no_extras:
         out = outlier_headline(args, qar, torch, np, synth, dev, "outliers", as_extra=True)
         result["outliers_step"] = {k: out[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
